@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and rounds them to bfloat16; it holds
+none of the attention arithmetic, so both the HIP path and the CPU oracle can
+take their inputs from it without sharing any of the method.
+
+Recipe (the same for every workload):
+
+* ``numpy.random.default_rng(seed)`` (PCG64);
+* float32 standard normal draws, in the order Q, K, V, then dO when the
+  workload has a backward pass, then (for the outlier workload) the outlier
+  channel indices, drawn without replacement;
+* outlier channels of Q and K are multiplied by the outlier factor in float32
+  before rounding (the FlashAttention-3 news page, section on FP8 and
+  incoherent processing, simulates activation outliers with a few
+  large-magnitude entries in N(0,1) data);
+* bfloat16 workloads round every float32 value once, round-to-nearest-even.
+
+Layouts are row-major: Q, dO are [B, Hq, Nq, d]; K, V are [B, Hkv, Nk, d].
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def round_to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Round float32 values to bfloat16, round-to-nearest-even.
+
+    Returns ``(values, bits)``: ``values`` is float32 holding exactly the
+    bfloat16 numbers, ``bits`` the uint16 bfloat16 encodings. Inputs are
+    finite (standard normal draws), so NaN handling is not needed here.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    r = (u + bias) & np.uint32(0xFFFF0000)
+    return r.view(np.float32), (r >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass
+class AttentionInputs:
+    """Host copies of one workload's inputs.
+
+    ``q``, ``k``, ``v``, ``do`` are float32 arrays holding the exact input
+    values (bfloat16-representable for bf16 workloads). ``*_bits`` hold the
+    uint16 bfloat16 encodings for bf16 workloads and are ``None`` for fp32.
+    """
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray | None
+    dtype: str
+    q_bits: np.ndarray | None = None
+    k_bits: np.ndarray | None = None
+    v_bits: np.ndarray | None = None
+    do_bits: np.ndarray | None = None
+    outlier_channels: np.ndarray | None = None
+
+
+def make_inputs(
+    seed: int,
+    batch: int,
+    n_q_heads: int,
+    n_kv_heads: int,
+    seqlen_q: int,
+    seqlen_k: int,
+    head_dim: int,
+    dtype: str = "bf16",
+    with_do: bool = False,
+    n_outlier_channels: int = 0,
+    outlier_factor: float = 20.0,
+) -> AttentionInputs:
+    """Draw one workload's inputs following the recipe in the module doc."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    rng = np.random.default_rng(seed)
+    qs = (batch, n_q_heads, seqlen_q, head_dim)
+    ks = (batch, n_kv_heads, seqlen_k, head_dim)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = rng.standard_normal(ks, dtype=np.float32)
+    do = rng.standard_normal(qs, dtype=np.float32) if with_do else None
+    channels = None
+    if n_outlier_channels:
+        channels = np.sort(rng.choice(head_dim, size=n_outlier_channels, replace=False))
+        f = np.float32(outlier_factor)
+        q[..., channels] *= f
+        k[..., channels] *= f
+    if dtype == "f32":
+        return AttentionInputs(q, k, v, do, dtype, outlier_channels=channels)
+    qv, qb = round_to_bf16(q)
+    kv, kb = round_to_bf16(k)
+    vv, vb = round_to_bf16(v)
+    if do is not None:
+        dov, dob = round_to_bf16(do)
+    else:
+        dov, dob = None, None
+    return AttentionInputs(qv, kv, vv, dov, dtype, qb, kb, vb, dob, channels)

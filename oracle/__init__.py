@@ -1,0 +1,14 @@
+"""CPU oracle for exact attention (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the library itself.
+"""
+
+from .attention import (  # noqa: F401
+    backward,
+    backward_head,
+    forward,
+    forward_head,
+    probabilities_head,
+    row_dot,
+)
