@@ -1,0 +1,25 @@
+"""Exact tiled attention (FlashAttention-2 order) for AMD MI355X / gfx950.
+
+The computation lives in libfa.so (C ABI, include/fa.h); this package holds
+the ctypes binding, the seeded input generator, the workload table and the
+build script.
+"""
+
+from .binding import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_F32,
+    FA_ERR_HIP,
+    FA_ERR_INVALID_ARGUMENT,
+    FA_ERR_UNSUPPORTED,
+    FA_OK,
+    FAError,
+    backward,
+    fa_bwd,
+    fa_bwd_workspace_bytes,
+    fa_fwd,
+    fa_last_error,
+    fa_status_string,
+    fa_version,
+    forward,
+    load_library,
+)

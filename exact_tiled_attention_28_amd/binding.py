@@ -1,0 +1,173 @@
+"""ctypes binding of libfa.so (include/fa.h). Argument marshalling only:
+every step of the attention computation runs in the library's HIP kernels.
+
+Two levels:
+
+* ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_workspace_bytes`` / ``fa_status_string``
+  / ``fa_last_error`` / ``fa_version`` mirror the C functions one to one
+  (pointers and streams as Python ints);
+* ``forward`` / ``backward`` take torch tensors on the GPU, allocate the
+  outputs with torch, call the C functions on torch's current stream and
+  raise ``FAError`` on a non-zero status.
+
+There is no fallback: if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+_lib = None
+
+_c_int = ctypes.c_int
+_c_ptr = ctypes.c_void_p
+_c_float = ctypes.c_float
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {fa_status_string(status)}: {detail}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} not found: build it with `python -m exact_tiled_attention_28_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(p)
+    lib.fa_fwd.restype = _c_int
+    lib.fa_fwd.argtypes = [_c_ptr] * 5 + [_c_int] * 6 + [_c_float] + [_c_int] * 3 + [_c_ptr]
+    lib.fa_bwd.restype = _c_int
+    lib.fa_bwd.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [_c_int]
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_version.restype = _c_int
+    lib.fa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# one-to-one wrappers of the C functions
+# ---------------------------------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim, scale, causal,
+           in_dtype, out_dtype, stream) -> int:
+    return load_library().fa_fwd(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim,
+                                 scale, causal, in_dtype, out_dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+           head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream) -> int:
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
+                                 seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
+                                 stream)
+
+
+def fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q) -> int:
+    return load_library().fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return load_library().fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return load_library().fa_version()
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor convenience layer (allocation and marshalling only)
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _torch_dtype(code):
+    import torch
+    return torch.float32 if code == FA_DTYPE_F32 else torch.bfloat16
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(rc, where):
+    if rc != FA_OK:
+        raise FAError(rc, where, fa_last_error())
+
+
+def forward(q, k, v, scale, causal, out_dtype=None, o=None, lse=None, stream=None):
+    """O, L = attention(q, k, v). q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]
+    (contiguous, bf16 or fp32, on the GPU). Returns (o, lse)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    oc = _dtype_code(q) if out_dtype is None else (FA_DTYPE_F32 if out_dtype == torch.float32 else FA_DTYPE_BF16)
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                float(scale), int(bool(causal)), _dtype_code(q), oc, _stream_handle(stream))
+    _check(rc, "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None):
+    """dQ (fp32), dK, dV (grad_dtype, default the input dtype) and the
+    workspace holding D. Returns (dq, dk, dv, dvec)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    gc = _dtype_code(q) if grad_dtype is None else (FA_DTYPE_F32 if grad_dtype == torch.float32 else FA_DTYPE_BF16)
+    dq = torch.empty((B, Hq, Nq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, Nk, d), dtype=_torch_dtype(gc), device=q.device)
+    dv = torch.empty((B, Hkv, Nk, d), dtype=_torch_dtype(gc), device=q.device)
+    ws = torch.empty(max(1, fa_bwd_workspace_bytes(B, Hq, Nq) // 4), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse, do):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
+    _check(rc, "fa_bwd")
+    return dq, dk, dv, ws[:B * Hq * Nq].view(B, Hq, Nq)

@@ -1,0 +1,105 @@
+// fa_api.cpp — the C ABI declared in include/fa.h: validate on the host,
+// pick the kernel instantiation, launch on the caller's stream, return.
+#include <cmath>
+#include <string>
+
+#include "../../include/fa.h"
+#include "fa_args.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int rc, const std::string& msg) {
+  g_last_error = msg;
+  return rc;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int n_q_heads,
+           int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal, int in_dtype,
+           int out_dtype, void* stream) {
+  std::string err;
+  const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
+  if (int rc = fa::check_fwd(q, k, v, o, lse, s, scale, causal, in_dtype, out_dtype, err)) return fail(rc, err);
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  hipError_t e = fa::launch_fwd(a, head_dim, in_dtype == FA_DTYPE_F32, causal != 0, out_dtype == FA_DTYPE_F32,
+                                (hipStream_t)stream);
+  return hip_status(e, "fa_fwd launch");
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
+           int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
+           void* stream) {
+  std::string err;
+  const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
+  if (int rc = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, s, scale, causal, in_dtype, o_dtype,
+                             grad_dtype, err))
+    return fail(rc, err);
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dvec = workspace;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
+                                (hipStream_t)stream);
+  return hip_status(e, "fa_bwd launch");
+}
+
+size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q) {
+  if (batch <= 0 || n_q_heads <= 0 || seqlen_q <= 0) return 0;
+  return (size_t)4 * (size_t)batch * (size_t)n_q_heads * (size_t)seqlen_q;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// fa_device.h — gfx950 device helpers shared by the attention kernels:
+// vector types, MFMA wrappers, the LDS chunk swizzle, bf16 packing and the
+// cross-half-wave exchange used by the row reductions.
+//
+// MFMA lane layouts used throughout (CDNA3/CDNA4 ISA, 32x32 output blocks):
+//   A operand (M x K): lane l holds row m = l % 32 and a set of K values that
+//                      depends only on the half-wave g = l / 32;
+//   B operand (K x N): lane l holds column n = l % 32 and the same K set;
+//   C (M x N, 16 fp32 per lane): lane l holds column n = l % 32 and rows
+//                      m = 8 * (r / 4) + 4 * g + (r % 4) for register r.
+// A and B use one common (half-wave, element) -> k numbering, so a product
+// only needs both operands to put the same k in the same slot; which physical
+// k that is does not matter. The kernels use this freedom to feed an
+// accumulator straight back as the next product's B operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short short4v;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// C += A * B, 32x32 output, K = 16, bf16 operands, fp32 accumulate.
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// C += A * B, 32x32 output, K = 2, fp32 operands, fp32 accumulate.
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Value of the same register in lane l ^ 32, combined with op; returns
+// op(x[l], x[l ^ 32]) in every lane.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_add(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round 8 fp32 values to bf16 (round-to-nearest-even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+  f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// LDS tiles hold rows of `row_chunks` 16-byte chunks. Chunk c of row r is
+// stored at chunk position c ^ swz(r) so that the 16 rows read together by
+// one MFMA operand fetch fall in distinct banks.
+template <int ROW_CHUNKS>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (ROW_CHUNKS >= 16) {
+    return row & 15;
+  } else {
+    return (row >> (4 - __builtin_ctz(ROW_CHUNKS))) & (ROW_CHUNKS - 1);
+  }
+}
+
+// Byte offset of (row, byte-in-row) inside a swizzled LDS tile.
+template <int ROW_CHUNKS>
+__device__ __forceinline__ int tile_off(int row, int byte_in_row) {
+  int c = byte_in_row >> 4;
+  return row * (ROW_CHUNKS * 16) + (((c ^ swz<ROW_CHUNKS>(row)) << 4) | (byte_in_row & 15));
+}
+
+}  // namespace fa

@@ -1,0 +1,311 @@
+// fa_fwd.hip — exact attention forward for gfx950, FlashAttention-2 order.
+//
+// Method (page "6.2 FlashAttention V2 chi tiết", sections 2.2, 3.2, 4.2, 5.3,
+// 6.1; CSDN FlashAttention-2 article, "前向传播" and "工作分区"):
+//   * one workgroup per (batch, query head, Q tile of BR rows); the Q tile is
+//     read from HBM once and stays in registers for the whole inner loop;
+//   * the inner loop streams K/V tiles of BC keys through double-buffered LDS
+//     and stops at the causal diagonal;
+//   * each wavefront owns 32 query rows of the Q tile and sees the whole K/V
+//     tile, so no softmax statistics are merged between wavefronts;
+//   * running row max m and row sum l; the output accumulator is left
+//     unnormalised and only rescaled by exp(m_old - m_new); one division by l
+//     at the end, and only L = m + ln(l) is written besides O;
+//   * tiles strictly above the diagonal are never visited; tiles that cross
+//     it are masked elementwise.
+//
+// gfx950 mapping. A wavefront computes S^T = K_j Q_i^T (keys x its 32
+// queries) with 32x32 MFMAs, so every lane holds one query column of the
+// scores: the row max and row sum are in-register reductions plus one
+// exchange between the two half-waves. The same lane layout lets the
+// probabilities, packed to bf16, serve directly as the B operand of the
+// second product O^T += V_j^T P^T, whose accumulator again keeps one query
+// per lane, so the rescale by exp(m_old - m_new) is a per-lane scalar
+// multiply. Softmax runs in base 2: scores are scaled by |scale| * log2(e)
+// in fp32 after the MFMA, and L is converted back to natural log on store.
+// A negative scale is folded into the sign of Q as it is loaded (exact).
+//
+// The fp32 path instantiates the same template with fp32 operands and the
+// 32x32x2 fp32 MFMA, so it checks the tiling logic at fp32 precision.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+template <bool F32IN, int D, int NW>
+struct FwdTile {
+  static constexpr int EB = F32IN ? 4 : 2;   // bytes per input element
+  static constexpr int BR = 32 * NW;         // query rows per workgroup
+  static constexpr int BC = F32IN ? 32 : 64; // keys per K/V tile
+  static constexpr int NKB = BC / 32;        // 32-key blocks per tile
+  static constexpr int ROWB = D * EB;        // bytes per K/V row
+  static constexpr int RC = ROWB / 16;       // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;    // bytes per K or V tile
+  static constexpr int NT = 64 * NW;         // threads per workgroup
+  static constexpr int CPT = BC * RC / NT;   // chunks per thread per tile
+  static_assert(BC * RC % NT == 0, "tile chunks must split evenly over threads");
+};
+
+template <bool F32IN, int D, bool CAUSAL, bool OUTF32, int NW>
+__global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
+  using T = FwdTile<F32IN, D, NW>;
+  constexpr int BR = T::BR, BC = T::BC, NKB = T::NKB, ROWB = T::ROWB, RC = T::RC, TILEB = T::TILEB;
+  constexpr int NT = T::NT, CPT = T::CPT;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Work decode: query heads vary fastest so that all heads' tiles of one
+  // rank are dispatched together; causal tiles go heaviest first. Heads that
+  // share a K/V head are B*Hkv apart, so with B*Hkv a multiple of 8 they land
+  // on the same XCD (dispatch is round-robin over the 8 XCDs).
+  const int heads = a.B * a.Hq;
+  const int slot = blockIdx.x % heads;
+  const int rank = blockIdx.x / heads;
+  const int bkv_n = a.B * a.Hkv;
+  const int bkv = slot % bkv_n;
+  const int member = slot / bkv_n;
+  const int b = bkv / a.Hkv;
+  const int hkv = bkv % a.Hkv;
+  const int hq = hkv * a.G + member;
+  const int qt = CAUSAL ? (a.n_q_tiles - 1 - rank) : rank;
+  const int q0 = qt * BR;
+  const int q0w = q0 + 32 * w;
+  const int qrow = q0w + l32;
+
+  const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
+  const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), loaded once ----------------
+  using QFrag = std::conditional_t<F32IN, float, bf16x8>;
+  constexpr int NQF = F32IN ? D / 2 : D / 16;
+  QFrag qf[NQF];
+  if constexpr (F32IN) {
+    const float* Qr = (const float*)a.q + (qhead + qrow) * D;
+    for (int kk = 0; kk < NQF; ++kk) {
+      float x = (qrow < a.Nq) ? Qr[2 * kk + g] : 0.0f;
+      qf[kk] = a.neg ? -x : x;
+    }
+  } else {
+    const char* Qr = (const char*)a.q + (qhead + qrow) * ROWB;
+    const unsigned sign = a.neg ? 0x80008000u : 0u;
+    for (int kk = 0; kk < NQF; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qrow < a.Nq) x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
+      x ^= sign;
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
+  const int n_kv = ceil_div(kv_end, BC);
+
+  // ---- K/V tile staging: HBM -> registers -> swizzled LDS -----------------
+  u32x4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int jt) {
+    const int kv0 = jt * BC;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = tid + NT * u;
+      const int row = ci / RC, c = ci % RC;
+      if (kv0 + row < a.Nk) {
+        const size_t off = (size_t)(kv0 + row) * ROWB + c * 16;
+        kr[u] = *(const u32x4*)(Kh + off);
+        vr[u] = *(const u32x4*)(Vh + off);
+      } else {
+        kr[u] = u32x4{0u, 0u, 0u, 0u};
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* Kt = smem + buf * 2 * TILEB;
+    char* Vt = Kt + TILEB;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ci = tid + NT * u;
+      const int row = ci / RC, c = ci % RC;
+      const int off = tile_off<RC>(row, c * 16);
+      *(u32x4*)(Kt + off) = kr[u];
+      *(u32x4*)(Vt + off) = vr[u];
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY;  // running max, log2 units (scaled scores)
+  float lsum = 0.0f;    // running sum over this half-wave's keys
+  const float c = a.c;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int jt = 0; jt < n_kv; ++jt) {
+    const int kv0 = jt * BC;
+    const bool has_next = jt + 1 < n_kv;
+    if (has_next) load_tile(jt + 1);
+    const char* Kt = smem + (jt & 1) * 2 * TILEB;
+    const char* Vt = Kt + TILEB;
+
+    // A wavefront whose 32 rows all lie above this tile skips it.
+    const bool active = !CAUSAL || kv0 <= q0w + 31;
+    if (active) {
+      // ---- S^T = K_j Q_i^T ------------------------------------------------
+      f32x16 sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = f32x16{};
+        const int krow = kb * 32 + l32;
+        if constexpr (F32IN) {
+#pragma unroll
+          for (int kk = 0; kk < NQF; ++kk) {
+            const float ka = *(const float*)(Kt + tile_off<RC>(krow, (2 * kk + g) * 4));
+            sacc[kb] = mfma_f32(ka, qf[kk], sacc[kb]);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < NQF; ++kk) {
+            const bf16x8 ka = *(const bf16x8*)(Kt + tile_off<RC>(krow, (kk * 16 + 8 * g) * 2));
+            sacc[kb] = mfma_bf16(ka, qf[kk], sacc[kb]);
+          }
+        }
+      }
+
+      // ---- mask (diagonal-crossing or ragged tiles only) --------------------
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
+            sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+          }
+      }
+
+      // ---- online softmax ---------------------------------------------------
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(sacc[kb][r], c, -m_new));
+          if (need_mask) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
+          sacc[kb][r] = p;
+          rs += p;
+        }
+      lsum = fmaf(alpha, lsum, rs);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+      // ---- O^T += V_j^T P^T -------------------------------------------------
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const float va = *(const float*)(Vt + tile_off<RC>(key, (db * 32 + l32) * 4));
+              oacc[db] = mfma_f32(va, sacc[kb][r], oacc[db]);
+            }
+          }
+      } else {
+        // Step t covers keys 16t..16t+15; slot (g, v) of both operands holds
+        // key 16t + 8*(v/4) + 4g + v%4, which is where the S^T accumulator
+        // registers 8*(t%2)..8*(t%2)+7 of block t/2 put it.
+#pragma unroll
+        for (int t = 0; t < BC / 16; ++t) {
+          float pv[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) pv[v] = sacc[t >> 1][8 * (t & 1) + v];
+          const bf16x8 pb = to_bf16x8(pv);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            bf16x8 va;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              const int key = 16 * t + 8 * (v >> 2) + 4 * g + (v & 3);
+              va[v] = *(const __bf16*)(Vt + tile_off<RC>(key, (db * 32 + l32) * 2));
+            }
+            oacc[db] = mfma_bf16(va, pb, oacc[db]);
+          }
+        }
+      }
+    }
+
+    if (has_next) store_tile((jt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
+  const float lt = half_swap_add(lsum);
+  const float inv = 1.0f / lt;
+  if (qrow < a.Nq) {
+    const size_t orow = (qhead + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = db * 32 + 8 * a4 + 4 * g;
+        f32x4 ov = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                    oacc[db][4 * a4 + 3] * inv};
+        if constexpr (OUTF32) {
+          *(f32x4*)((float*)a.o + orow + d0) = ov;
+        } else {
+          *(bf16x4*)((__bf16*)a.o + orow + d0) = __builtin_convertvector(ov, bf16x4);
+        }
+      }
+    if (g == 0) a.lse[qhead + qrow] = (m + fast_log2(lt)) * kLn2;
+  }
+}
+
+template <bool F32IN, int D, bool CAUSAL, bool OUTF32>
+static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
+  constexpr int NW = 4;
+  using T = FwdTile<F32IN, D, NW>;
+  a.n_q_tiles = ceil_div(a.Nq, T::BR);
+  const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
+  hipLaunchKernelGGL((fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW>), dim3((unsigned)blocks), dim3(T::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool F32IN, int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, bool out_f32, hipStream_t s) {
+  if (causal) return out_f32 ? launch_fwd_t<F32IN, D, true, true>(a, s) : launch_fwd_t<F32IN, D, true, false>(a, s);
+  return out_f32 ? launch_fwd_t<F32IN, D, false, true>(a, s) : launch_fwd_t<F32IN, D, false, false>(a, s);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool in_f32, bool causal, bool out_f32, hipStream_t s) {
+  if (in_f32) {
+    return head_dim == 64 ? launch_fwd_d<true, 64>(a, causal, out_f32, s)
+                          : launch_fwd_d<true, 128>(a, causal, out_f32, s);
+  }
+  return head_dim == 64 ? launch_fwd_d<false, 64>(a, causal, out_f32, s)
+                        : launch_fwd_d<false, 128>(a, causal, out_f32, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,135 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,   L = per-row logsumexp,
+ * and its gradients, tile by tile with online softmax in the FlashAttention-2
+ * order: one workgroup per Q tile (page "6.2 FlashAttention V2 chi tiết",
+ * sections 2.2 and 6.1), K/V tiles streamed through LDS, an unnormalised output
+ * rescaled only by exp(m_old - m_new) and divided once at the end (section
+ * 3.2), causal tiles above the diagonal skipped (section 5.3), and a backward
+ * pass that owns one K/V column block per workgroup and adds dQ atomically
+ * (section 7.2; CSDN FlashAttention-2 article, "并行性 / 反向传播").
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory)
+ *    on the device that is current when the call is made.
+ *  - Layout is contiguous row-major "BHSD": Q, O, dO, dQ are
+ *    [batch][n_q_heads][seqlen_q][head_dim]; K, V, dK, dV are
+ *    [batch][n_kv_heads][seqlen_k][head_dim]; L (lse) and D are
+ *    [batch][n_q_heads][seqlen_q].
+ *  - Grouped-query attention: G = n_q_heads / n_kv_heads query heads share one
+ *    K/V head, and query head h uses K/V head h / G (contiguous groups; the
+ *    CSDN article, "多查询注意力和分组查询注意力").
+ *  - Base pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it; the call returns without synchronising.
+ *  - Ownership: the caller allocates and frees every buffer and owns the
+ *    stream. The library never allocates, frees or synchronises, and keeps no
+ *    state between calls except a thread-local error message.
+ *  - Errors: argument problems are detected on the host before anything is
+ *    enqueued, and leave every output untouched. A launch failure returns
+ *    FA_ERR_HIP. Faults inside a kernel surface at the caller's next
+ *    synchronisation, as usual for HIP.
+ *  - Numerics: fp32 accumulation; probabilities P and dS are rounded to
+ *    bfloat16 (round-to-nearest-even) before the bf16 matrix products; the
+ *    scale is applied in fp32 to the fp32 scores, never folded into a rounded
+ *    operand. NaN or Inf in an input row propagates to the outputs that
+ *    depend on it.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad sizes, non-finite scale */
+  FA_ERR_UNSUPPORTED = 2,      /* head_dim, dtype combination, causal with seqlen_q != seqlen_k */
+  FA_ERR_HIP = 3               /* a HIP launch failed; fa_last_error() has the text */
+};
+
+/* Element types. */
+enum fa_dtype {
+  FA_DTYPE_F32 = 0,
+  FA_DTYPE_BF16 = 1
+};
+
+/*
+ * fa_fwd — exact attention forward (page "6.2 FlashAttention V2 chi tiết",
+ * section 6.1; CSDN FlashAttention-2 article, "前向传播").
+ *
+ *   q        [B][Hq][Nq][d]  in_dtype, read only
+ *   k, v     [B][Hkv][Nk][d] in_dtype, read only
+ *   o        [B][Hq][Nq][d]  out_dtype, fully overwritten:
+ *            O = softmax(scale * Q K^T, causal mask) V
+ *   lse      [B][Hq][Nq] fp32, fully overwritten: L_i = m_i + ln(l_i), the
+ *            natural-log logsumexp of the scaled (masked) scores of row i
+ *            (page 6.2, sections 6.1 and 7.1)
+ *   batch, n_q_heads, n_kv_heads  >= 1, n_q_heads % n_kv_heads == 0
+ *   seqlen_q, seqlen_k            >= 1; causal requires seqlen_q == seqlen_k
+ *   head_dim                      64 or 128
+ *   scale    any finite float (0 allowed); typically 1/sqrt(head_dim)
+ *   causal   0 or 1: query i attends to keys j <= i (page 6.2, section 5.1)
+ *   in_dtype  FA_DTYPE_BF16 (MFMA bf16 path) or FA_DTYPE_F32 (fp32 MFMA path,
+ *             for checking the tiling at fp32 precision)
+ *   out_dtype FA_DTYPE_BF16 or FA_DTYPE_F32 (any combination with in_dtype)
+ *   stream   hipStream_t or NULL
+ * Returns FA_OK or an fa_status code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int batch, int n_q_heads, int n_kv_heads, int seqlen_q, int seqlen_k,
+           int head_dim, float scale, int causal, int in_dtype, int out_dtype,
+           void* stream);
+
+/*
+ * fa_bwd — exact attention backward (page "6.2 FlashAttention V2 chi tiết",
+ * section 7; CSDN FlashAttention-2 article, "3.1.2 反向传播公式解析"):
+ *   D = rowsum(dO o O); P = exp(scale * Q K^T - L) (masked);
+ *   dV = P^T dO; dP = dO V^T; dS = P o (dP - D);
+ *   dQ = scale * dS K; dK = scale * dS^T Q;
+ * with dK, dV summed over the query heads of each K/V head group.
+ *
+ *   q, dout  [B][Hq][Nq][d] in_dtype (must be FA_DTYPE_BF16), read only
+ *   k, v     [B][Hkv][Nk][d] in_dtype, read only
+ *   o        [B][Hq][Nq][d] o_dtype (bf16 or fp32), the forward output
+ *   lse      [B][Hq][Nq] fp32, the forward logsumexp
+ *   dq       [B][Hq][Nq][d] fp32, fully overwritten (zeroed, then accumulated
+ *            atomically across K/V column blocks; the last bits depend on the
+ *            order of the atomic adds)
+ *   dk, dv   [B][Hkv][Nk][d] grad_dtype (bf16 or fp32), fully overwritten
+ *   workspace  device buffer of at least fa_bwd_workspace_bytes() bytes; on
+ *            return it holds D as fp32 [B][Hq][Nq]
+ *   other arguments as in fa_fwd.
+ * Returns FA_OK or an fa_status code.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, float* dq, void* dk, void* dv,
+           float* workspace, int batch, int n_q_heads, int n_kv_heads,
+           int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+           int in_dtype, int o_dtype, int grad_dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: 4 * batch * n_q_heads * seqlen_q
+ * (the fp32 vector D, page 6.2 section 7.3). Returns 0 for non-positive
+ * arguments. */
+size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library ABI version, currently 1. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
