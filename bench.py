@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (bf16 O, fp32 L) followed by fa_bwd (D preprocess + main kernel,
+fp32 dQ, bf16 dK/dV) on the causal bf16 workload B=8, H=16, N=2048, d=128
+(seed 2), inputs resident in HBM. Prints ONE JSON line.
+
+value = causal-adjusted TFLOPS of the step: forward 4*B*H*N^2*d/2 plus
+backward 2.5x that, divided by the step time. Forward and backward TFLOPS
+and their fractions of the dense bf16 MFMA peak are reported separately.
+
+`roofline` covers the call that takes the most time per step, timed with HIP
+events recorded on the stream the library launches on. `cpu_baseline` times
+the fp64 CPU oracle (forward + backward) on a bounded sample of the same
+workload: a few (batch, head) slices.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --workload NAME   (one of the named workloads, extra)
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_tiled_attention_28_amd import binding  # noqa: E402
+from exact_tiled_attention_28_amd.inputs import make_inputs  # noqa: E402
+from exact_tiled_attention_28_amd.workloads import (  # noqa: E402
+    MI355X_BF16_PEAK_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, bwd_bytes, bwd_flops, fwd_bytes, fwd_flops)
+
+METRIC = "attention fwd/bwd TFLOPS (causal-adjusted) and % of MI355X bf16 MFMA peak"
+STEP_WORKLOAD = "fwd_bf16_causal_b8_h16_n2048_d128"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
+    p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
+    return p.parse_args()
+
+
+def device_inputs(w, with_do):
+    import torch
+    inp = make_inputs(w.seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim, w.dtype,
+                      with_do=with_do, n_outlier_channels=w.n_outlier_channels)
+
+    def up(bits, vals):
+        if w.dtype == "bf16":
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(vals).cuda()
+
+    q = up(inp.q_bits, inp.q)
+    k = up(inp.k_bits, inp.k)
+    v = up(inp.v_bits, inp.v)
+    do = up(inp.do_bits, inp.do) if with_do else None
+    return inp, q, k, v, do
+
+
+class Step:
+    """The hot path with every output buffer allocated once, up front."""
+
+    def __init__(self, w, q, k, v, do):
+        import torch
+        self.w = w
+        self.q, self.k, self.v, self.do = q, k, v, do
+        B, Hq, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.head_dim
+        dev = q.device
+        self.o = torch.empty((B, Hq, N, d), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        self.dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+        self.dk = torch.empty((B, Hkv, N, d), dtype=q.dtype, device=dev)
+        self.dv = torch.empty((B, Hkv, N, d), dtype=q.dtype, device=dev)
+        self.ws = torch.empty(binding.fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=dev)
+        self.code = binding.FA_DTYPE_BF16 if w.dtype == "bf16" else binding.FA_DTYPE_F32
+        self.stream = torch.cuda.current_stream()
+        self.sh = self.stream.cuda_stream
+
+    def fwd(self):
+        w = self.w
+        rc = binding.fa_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                            self.lse.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
+                            w.head_dim, w.scale, int(w.causal), self.code, self.code, self.sh)
+        if rc:
+            raise binding.FAError(rc, "fa_fwd", binding.fa_last_error())
+
+    def bwd(self):
+        w = self.w
+        rc = binding.fa_bwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                            self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
+                            self.dv.data_ptr(), self.ws.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen,
+                            w.seqlen, w.head_dim, w.scale, int(w.causal), self.code, self.code, self.code,
+                            self.sh)
+        if rc:
+            raise binding.FAError(rc, "fa_bwd", binding.fa_last_error())
+
+
+def time_calls(step, calls, steps, warmup):
+    """Run `calls` (a list of callables) per step; return the step times and
+    per-call times (ms) from HIP events recorded on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(step.stream)
+        for i, c in enumerate(calls):
+            c()
+            ev[s][i + 1].record(step.stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per_call = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(calls))] for s in range(steps)])
+    per_step = per_call.sum(axis=1)
+    return per_step, per_call, wall
+
+
+def cpu_baseline(w, inp, heads):
+    """The fp64 oracle, untuned, on `heads` (batch, head) slices of the
+    workload: forward + backward. Returns the JSON object."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    sel = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)][:heads]
+    t0 = time.perf_counter()
+    for b, h in sel:
+        g = h // w.group
+        oracle.forward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], w.scale, w.causal)
+        oracle.backward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], inp.do[b, h], w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = heads * (fwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal)
+                     + bwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal))
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of {heads} of {w.batch * w.n_q_heads} (batch, head) slices "
+                      f"(N={w.seqlen}, d={w.head_dim}, causal), {dt:.1f} s wall, same causal-adjusted flop count"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the attention path has no multi-GPU mode; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load_library()
+
+    if args.workload:
+        return bench_one(args)
+
+    w = WORKLOADS[STEP_WORKLOAD]
+    inp, q, k, v, do = device_inputs(w, with_do=True)
+    if do is None:
+        raise RuntimeError("dO missing")
+    step = Step(w, q, k, v, do)
+    per_step, per_call, wall = time_calls(step, [step.fwd, step.bwd], args.steps, args.warmup)
+    ms_step = float(np.median(per_step))
+    ms_fwd = float(np.median(per_call[:, 0]))
+    ms_bwd = float(np.median(per_call[:, 1]))
+    ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    bf = bwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
+    fwd_tf = ff / (ms_fwd * 1e-3) / 1e12
+    bwd_tf = bf / (ms_bwd * 1e-3) / 1e12
+    avg_fwd = float(np.mean(per_call[:, 0]))
+    avg_bwd = float(np.mean(per_call[:, 1]))
+    if avg_bwd >= avg_fwd:
+        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_kernel, one call)", "flops": bf, "ms": avg_bwd}
+    else:
+        dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd}
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fa_fwd + fa_bwd, bf16, causal, B=8 Hq=Hkv=16 N=2048 d=128 (seed 2)",
+                   "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "seqlen": w.seqlen, "head_dim": w.head_dim, "causal": w.causal, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * tflops / MI355X_BF16_PEAK_TFLOPS, 2),
+        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_tf, 2),
+                "pct_of_bf16_peak": round(100 * fwd_tf / MI355X_BF16_PEAK_TFLOPS, 2),
+                "gbps_algorithmic": round(fwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
+                                                    w.head_dim) / (ms_fwd * 1e-3) / 1e9, 1)},
+        "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_tf, 2),
+                "pct_of_bf16_peak": round(100 * bwd_tf / MI355X_BF16_PEAK_TFLOPS, 2),
+                "gbps_algorithmic": round(bwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
+                                                    w.head_dim) / (ms_bwd * 1e-3) / 1e9, 1)},
+        "wall_ms_per_step": round(wall, 4),
+        "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(dom["ms"], 4)},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def bench_one(args):
+    """Time one named workload's pass (fwd or bwd); prints one JSON line."""
+    w = WORKLOADS[args.workload]
+    inp, q, k, v, do = device_inputs(w, with_do=w.passes == "bwd")
+    step = Step(w, q, k, v, do if do is not None else q)
+    if w.passes == "bwd":
+        step.fwd()
+        calls, fl = [step.bwd], bwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+        by = bwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim)
+    else:
+        calls, fl = [step.fwd], fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+        eb = 4 if w.dtype == "f32" else 2
+        by = fwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim, eb, eb)
+    per_step, _, _ = time_calls(step, calls, args.steps, args.warmup)
+    ms = float(np.median(per_step))
+    tf = fl / (ms * 1e-3) / 1e12
+    print(json.dumps({"workload": w.name, "ms": round(ms, 4), "ms_min": round(float(per_step.min()), 4),
+                      "tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / MI355X_BF16_PEAK_TFLOPS, 2),
+                      "gbps_algorithmic": round(by / (ms * 1e-3) / 1e9, 1),
+                      "pct_of_hbm": round(100 * by / (ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 2)}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,5 +1,425 @@
-// fa_bwd.hip — placeholder until the backward kernels land.
+// fa_bwd.hip — exact attention backward for gfx950, FlashAttention-2 order.
+//
+// Method (page "6.2 FlashAttention V2 chi tiết", section 7; CSDN
+// FlashAttention-2 article, "3.1.2 反向传播公式解析", "并行性 / 反向传播"):
+//   1. a separate preprocess kernel computes D = rowsum(dO o O) once and
+//      zeroes the fp32 dQ accumulator (page 6.2, section 7.3);
+//   2. the main kernel gives each workgroup one K/V column block j; it walks
+//      every query head of the K/V head's group and every Q block i that can
+//      see block j, recomputing P = exp(scale * Q_i K_j^T - L_i) from the
+//      saved logsumexp (page 6.2, section 7.1), and accumulates
+//        dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P o (dP - D_i),
+//        dK_j += dS^T Q_i  (privately, in registers, so no atomics),
+//        dQ_i += dS K_j    (added atomically to fp32 dQ in HBM, since many
+//                           column blocks contribute to one Q block);
+//      dQ and dK carry the factor `scale` of S = scale * Q K^T (chain rule).
+//
+// gfx950 mapping. The four wavefronts of a workgroup split the K/V block by
+// keys (32 each), so dK and dV rows are private to one wavefront. Each
+// wavefront computes S = Q_i K_j^T and dP = dO_i V_j^T as 32x32 blocks with
+// one key per lane; K_j and V_j stay in registers as the B operands. The same
+// accumulator layout is the B operand of dV^T += dO_i^T P and
+// dK^T += Q_i^T dS, whose A operands are read from the LDS tiles of dO_i and
+// Q_i with the gfx950 transpose read (ds_read_b64_tr_b16). dS is staged in
+// LDS, transposed by key, and dQ_i = dS K_j is computed with both operands
+// read by transpose reads, then added to HBM with fp32 atomics (lanes cover
+// contiguous head-dim columns, so each atomic instruction touches whole
+// cache lines).
+#include <type_traits>
+
+#include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_tiles.h"
+
 namespace fa {
-hipError_t launch_bwd(const BwdArgs&, int, bool, bool, bool, hipStream_t) { return hipErrorNotSupported; }
+
+// ---------------------------------------------------------------------------
+// preprocess: D = rowsum(dO o O), dQ = 0
+// ---------------------------------------------------------------------------
+
+template <int D, bool OF32>
+__global__ void __launch_bounds__(256) bwd_preprocess_kernel(const __bf16* __restrict__ dout, const void* __restrict__ o,
+                                                             float* __restrict__ dvec, float* __restrict__ dq,
+                                                             long long rows) {
+  constexpr int LPR = D / 8;  // lanes per row: 8 elements each
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / LPR;
+  const int part = (int)(t % LPR);
+  float acc = 0.0f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + part * 8;
+    const u32x4 dv = *(const u32x4*)(dout + base);
+    const bf16x8 db = __builtin_bit_cast(bf16x8, dv);
+    f32x8 of;
+    if constexpr (OF32) {
+      const f32x4 a = *(const f32x4*)((const float*)o + base);
+      const f32x4 b = *(const f32x4*)((const float*)o + base + 4);
+      of = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+      const u32x4 ov = *(const u32x4*)((const __bf16*)o + base);
+      of = __builtin_convertvector(__builtin_bit_cast(bf16x8, ov), f32x8);
+    }
+    const f32x8 df = __builtin_convertvector(db, f32x8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(df[e], of[e], acc);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)(dq + base) = z;
+    *(f32x4*)(dq + base + 4) = z;
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
+  if (row < rows && part == 0) dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// main backward kernel
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct BwdTile {
+  static constexpr int NW = 4;
+  static constexpr int BKV = 32 * NW;  // keys per workgroup (32 per wavefront)
+  static constexpr int BQ = 64;        // query rows per step
+  static constexpr int QROWB = D * 2;  // bytes per Q / dO row
+  static constexpr int QRC = QROWB / 16;
+  static constexpr int QTILEB = BQ * QROWB;
+  static constexpr int KTILEB = BKV * QROWB;
+  static constexpr int SROWB = BQ * 2;  // dS^T row: BQ bf16
+  static constexpr int SRC = SROWB / 16;
+  static constexpr int STILEB = BKV * SROWB;
+  static constexpr int NT = 64 * NW;
+  static constexpr int QCPT = BQ * QRC / NT;  // Q (and dO) chunks per thread
+  static constexpr int KCPT = BKV * QRC / NT;
+  static constexpr int NDQ = (BQ / 32) * (D / 32) / NW;  // dQ 32x32 blocks per wave
+  // LDS carve-up (bytes)
+  static constexpr int OFF_Q = 0;                         // [2][QTILEB]
+  static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;       // [2][QTILEB]
+  static constexpr int OFF_K = OFF_DO + 2 * QTILEB;       // [KTILEB]
+  static constexpr int OFF_S = OFF_K + KTILEB;            // [STILEB]
+  static constexpr int OFF_L = OFF_S + STILEB;            // [2][BQ] fp32 (L * log2 e)
+  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;        // [2][BQ] fp32
+  static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
+  static_assert(BQ * QRC % NT == 0 && BKV * QRC % NT == 0, "tiles must split evenly");
+  static_assert(NDQ >= 1, "dQ blocks per wave");
+};
+
+// Transpose read of 4 bf16 down a column: lane (16-lane block b, index i)
+// gets rows row0(g) + e, e = 0..3, of column col0 + i, given that each lane
+// supplies the address of 4 consecutive columns of one row (verified on
+// gfx950: result[i][e] = loaded[4e + i/4][i%4] within each 16-lane block).
+template <int RC>
+__device__ __forceinline__ short4v tr_read(const char* tile, int row_base, int col_base_elems, int lane) {
+  const int j = lane & 15;
+  const int row = row_base + (j >> 2);
+  const int col = col_base_elems + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const char* p = tile + tile_off<RC>(row, col * 2);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat4(short4v a, short4v b) {
+  typedef __attribute__((ext_vector_type(8))) short short8v;
+  short8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int D, bool CAUSAL, bool GF32>
+__global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
+  using T = BwdTile<D>;
+  constexpr int BKV = T::BKV, BQ = T::BQ, QROWB = T::QROWB, QRC = T::QRC, QTILEB = T::QTILEB, SRC = T::SRC;
+  constexpr int NT = T::NT, QCPT = T::QCPT, KCPT = T::KCPT, NDQ = T::NDQ;
+  constexpr int NKK = D / 16;  // K-steps of the S / dP products
+  constexpr int NDB = D / 32;  // 32-column blocks of the head dim
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const sQ = smem + T::OFF_Q;
+  char* const sDO = smem + T::OFF_DO;
+  char* const sK = smem + T::OFF_K;
+  char* const sS = smem + T::OFF_S;
+  float* const sL = (float*)(smem + T::OFF_L);
+  float* const sD = (float*)(smem + T::OFF_D);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Work decode: (batch, kv head) fastest, K/V blocks from the first (the
+  // heaviest under the causal mask) to the last.
+  const int bkv_n = a.B * a.Hkv;
+  const int bkv = blockIdx.x % bkv_n;
+  const int jblk = blockIdx.x / bkv_n;
+  const int b = bkv / a.Hkv;
+  const int hkv = bkv % a.Hkv;
+  const int kv0 = jblk * BKV;
+  const int key_l = 32 * w + l32;  // this lane's key inside the block
+  const int key = kv0 + key_l;
+
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  const char* __restrict__ Kh = (const char*)a.k + kvhead * QROWB;
+  const char* __restrict__ Vh = (const char*)a.v + kvhead * QROWB;
+
+  // K_j, V_j rows of this lane's key as B operands (K^T and V^T columns).
+  bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < a.Nk) {
+      x = *(const u32x4*)(Kh + (size_t)key * QROWB + (kk * 16 + 8 * g) * 2);
+      y = *(const u32x4*)(Vh + (size_t)key * QROWB + (kk * 16 + 8 * g) * 2);
+    }
+    kf[kk] = __builtin_bit_cast(bf16x8, x);
+    vf[kk] = __builtin_bit_cast(bf16x8, y);
+  }
+  // K_j tile in LDS for the dQ product.
+#pragma unroll
+  for (int u = 0; u < KCPT; ++u) {
+    const int ci = tid + NT * u;
+    const int row = ci / QRC, c = ci % QRC;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (kv0 + row < a.Nk) x = *(const u32x4*)(Kh + (size_t)(kv0 + row) * QROWB + c * 16);
+    *(u32x4*)(sK + tile_off<QRC>(row, c * 16)) = x;
+  }
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  const int n_qblk = ceil_div(a.Nq, BQ);
+  const int i_first = first_q_tile_for(kv0, BQ, CAUSAL);
+  const int n_i = n_qblk - i_first;
+  const int total = a.G * n_i;
+  const float c = a.c;
+  const float scale = a.scale;
+
+  // ---- Q_i / dO_i / L_i / D_i staging --------------------------------------
+  u32x4 qr[QCPT], dor[QCPT];
+  float lr = 0.0f, dr = 0.0f;
+  auto load_q = [&](int it) {
+    const int hm = it / n_i;
+    const int i = i_first + it % n_i;
+    const int hq = hkv * a.G + hm;
+    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    const int q0 = i * BQ;
+    const char* Qh = (const char*)a.q + qhead * QROWB;
+    const char* Oh = (const char*)a.dout + qhead * QROWB;
+#pragma unroll
+    for (int u = 0; u < QCPT; ++u) {
+      const int ci = tid + NT * u;
+      const int row = ci / QRC, cc = ci % QRC;
+      if (q0 + row < a.Nq) {
+        const size_t off = (size_t)(q0 + row) * QROWB + cc * 16;
+        qr[u] = *(const u32x4*)(Qh + off);
+        dor[u] = *(const u32x4*)(Oh + off);
+      } else {
+        qr[u] = u32x4{0u, 0u, 0u, 0u};
+        dor[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < BQ) {
+      const bool ok = q0 + tid < a.Nq;
+      // Rows past the end get L = +inf, so P = exp2(S c - inf) = 0 there.
+      lr = ok ? a.lse[qhead + q0 + tid] * kLog2e : INFINITY;
+      dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
+    }
+  };
+  auto store_q = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < QCPT; ++u) {
+      const int ci = tid + NT * u;
+      const int row = ci / QRC, cc = ci % QRC;
+      const int off = tile_off<QRC>(row, cc * 16);
+      *(u32x4*)(sQ + buf * QTILEB + off) = qr[u];
+      *(u32x4*)(sDO + buf * QTILEB + off) = dor[u];
+    }
+    if (tid < BQ) {
+      sL[buf * BQ + tid] = lr;
+      sD[buf * BQ + tid] = dr;
+    }
+  };
+
+  if (total > 0) {
+    load_q(0);
+    store_q(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    const int hm = it / n_i;
+    const int i = i_first + it % n_i;
+    const int hq = hkv * a.G + hm;
+    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    const int q0 = i * BQ;
+    const bool has_next = it + 1 < total;
+    if (has_next) load_q(it + 1);
+
+    const char* tQ = sQ + buf * QTILEB;
+    const char* tDO = sDO + buf * QTILEB;
+    const float* tL = sL + buf * BQ;
+    const float* tD = sD + buf * BQ;
+
+    // A wavefront whose keys all lie after every query of this block skips
+    // the products; its dS^T rows are written as zeros.
+    const bool active = !CAUSAL || kv0 + 32 * w <= q0 + BQ - 1;
+    f32x16 ds[BQ / 32];
+    if (active) {
+      // ---- S = Q_i K_j^T and dP = dO_i V_j^T (one key per lane) -----------
+      f32x16 s[BQ / 32], dp[BQ / 32];
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int off = tile_off<QRC>(qb * 32 + l32, (kk * 16 + 8 * g) * 2);
+          const bf16x8 qa = *(const bf16x8*)(tQ + off);
+          const bf16x8 oa = *(const bf16x8*)(tDO + off);
+          s[qb] = mfma_bf16(qa, kf[kk], s[qb]);
+          dp[qb] = mfma_bf16(oa, vf[kk], dp[qb]);
+        }
+      }
+      // ---- P = exp2(S c - L log2 e), dS = P o (dP - D) ----------------------
+      const bool need_mask = (CAUSAL && kv0 + 32 * w + 31 > q0) || (kv0 + 32 * w + 32 > a.Nk);
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int r0 = qb * 32 + 8 * a4 + 4 * g;
+          const f32x4 lv = *(const f32x4*)(tL + r0);
+          const f32x4 dv = *(const f32x4*)(tD + r0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * a4 + e;
+            float p = fast_exp2(fmaf(s[qb][r], c, -lv[e]));
+            if (need_mask) {
+              const bool vis = key < a.Nk && (!CAUSAL || key <= q0 + r0 + e);
+              p = vis ? p : 0.0f;
+            }
+            s[qb][r] = p;
+            ds[qb][r] = p * (dp[qb][r] - dv[e]);
+          }
+        }
+      // ---- dV^T += dO_i^T P and dK^T += Q_i^T dS -----------------------------
+#pragma unroll
+      for (int t = 0; t < BQ / 16; ++t) {
+        float pv[8], sv[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          pv[v] = s[t >> 1][8 * (t & 1) + v];
+          sv[v] = ds[t >> 1][8 * (t & 1) + v];
+        }
+        const bf16x8 pb = to_bf16x8(pv);
+        const bf16x8 sb = to_bf16x8(sv);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int rb = 16 * t + 4 * ((lane >> 5) & 1);
+          const bf16x8 doa = cat4(tr_read<QRC>(tDO, rb, db * 32, lane), tr_read<QRC>(tDO, rb + 8, db * 32, lane));
+          const bf16x8 qa = cat4(tr_read<QRC>(tQ, rb, db * 32, lane), tr_read<QRC>(tQ, rb + 8, db * 32, lane));
+          dvacc[db] = mfma_bf16(doa, pb, dvacc[db]);
+          dkacc[db] = mfma_bf16(qa, sb, dkacc[db]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) ds[qb] = f32x16{};
+    }
+
+    // ---- stage dS^T (keys x queries, bf16) ----------------------------------
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 x = {ds[qb][4 * a4], ds[qb][4 * a4 + 1], ds[qb][4 * a4 + 2], ds[qb][4 * a4 + 3]};
+        const int col = qb * 32 + 8 * a4 + 4 * g;
+        *(bf16x4*)(sS + tile_off<SRC>(key_l, col * 2)) = __builtin_convertvector(x, bf16x4);
+      }
+    __syncthreads();
+
+    // ---- dQ_i += scale * dS K_j (fp32 atomics) ------------------------------
+#pragma unroll
+    for (int u = 0; u < NDQ; ++u) {
+      const int bi = w + T::NW * u;
+      const int qb = bi / NDB, db = bi % NDB;
+      f32x16 acc = f32x16{};
+      const bool any = !CAUSAL || q0 + qb * 32 + 31 >= kv0;
+      if (any) {
+#pragma unroll
+        for (int t = 0; t < BKV / 16; ++t) {
+          const int rb = 16 * t + 4 * ((lane >> 5) & 1);
+          const bf16x8 sa = cat4(tr_read<SRC>(sS, rb, qb * 32, lane), tr_read<SRC>(sS, rb + 8, qb * 32, lane));
+          const bf16x8 kb = cat4(tr_read<QRC>(sK, rb, db * 32, lane), tr_read<QRC>(sK, rb + 8, db * 32, lane));
+          acc = mfma_bf16(sa, kb, acc);
+        }
+        float* dqh = a.dq + qhead * D;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (qrow < a.Nq) atomicAdd(dqh + (size_t)qrow * D + db * 32 + l32, scale * acc[r]);
+        }
+      }
+    }
+
+    if (has_next) store_q(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T, one key per lane ------------
+  if (key < a.Nk) {
+    const size_t rowoff = (kvhead + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = db * 32 + 8 * a4 + 4 * g;
+        const f32x4 kv = {scale * dkacc[db][4 * a4], scale * dkacc[db][4 * a4 + 1], scale * dkacc[db][4 * a4 + 2],
+                          scale * dkacc[db][4 * a4 + 3]};
+        const f32x4 vv = {dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]};
+        if constexpr (GF32) {
+          *(f32x4*)((float*)a.dk + rowoff + d0) = kv;
+          *(f32x4*)((float*)a.dv + rowoff + d0) = vv;
+        } else {
+          *(bf16x4*)((__bf16*)a.dk + rowoff + d0) = __builtin_convertvector(kv, bf16x4);
+          *(bf16x4*)((__bf16*)a.dv + rowoff + d0) = __builtin_convertvector(vv, bf16x4);
+        }
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
+  using T = BwdTile<D>;
+  auto kern = bwd_kernel<D, CAUSAL, GF32>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::NT), T::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
+  const long long rows = (long long)a.B * a.Hq * a.Nq;
+  const long long threads = rows * (D / 8);
+  const unsigned pblocks = (unsigned)((threads + 255) / 256);
+  if (o_f32)
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D, true>), dim3(pblocks), dim3(256), 0, s, (const __bf16*)a.dout, a.o,
+                       a.dvec, a.dq, rows);
+  else
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D, false>), dim3(pblocks), dim3(256), 0, s, (const __bf16*)a.dout, a.o,
+                       a.dvec, a.dq, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (causal) return grad_f32 ? launch_bwd_main<D, true, true>(a, s) : launch_bwd_main<D, true, false>(a, s);
+  return grad_f32 ? launch_bwd_main<D, false, true>(a, s) : launch_bwd_main<D, false, false>(a, s);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
+  return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, s)
+                        : launch_bwd_d<128>(a, causal, o_f32, grad_f32, s);
+}
+
 }  // namespace fa

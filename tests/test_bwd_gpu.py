@@ -1,0 +1,121 @@
+"""Backward parity on the GPU: fa_bwd (through the C ABI) against the fp64
+oracle's analytic gradients on the same seeded inputs.
+
+The backward is fed O and L from fa_fwd with fp32 O (the backward's D is
+rowsum(dO o O), so a bf16-rounded O would add its rounding to D; parity runs
+request fp32 outputs from the same kernels).
+
+Bounds. On the five named workloads (test_workloads_gpu.py) the bound is
+max-abs 1e-2 on dQ, dK, dV. On the extra shapes here (grouped heads summed,
+short causal rows with O(1) probabilities) the kernel's own rounding can
+exceed a flat 1e-2, so the bound is 1e-2 plus the worst case of that
+rounding: P and dS are rounded to bf16 (RNE, relative error <= 2^-9) before
+the dV, dK and dQ products, so
+    |err dV_jc| <= 2^-9 * sum_{h,i} |P_hij| |dO_hic|,
+    |err dK_jc| <= 2^-9 * s * sum_{h,i} |dS_hij| |Q_hic|,
+    |err dQ_ic| <= 2^-9 * s * sum_j |dS_ij| |K_jc|,
+computed here from the oracle's P. bf16 dK, dV outputs add half a bf16 ulp.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_tiled_attention_28_amd import binding
+from tests.gpu_util import announce, bf16_half_ulp, gen, host, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+U_BF16 = 2.0 ** -9
+
+
+def rounding_bounds(inp, scale, causal):
+    """Worst-case effect of rounding P and dS to bf16 (see module doc)."""
+    q, k, v, do = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    bq = np.zeros_like(q)
+    bk = np.zeros_like(k)
+    bv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            P = oracle.probabilities_head(q[b, h], k[b, g], scale, causal)
+            O = P @ v[b, g]
+            dS = P * (do[b, h] @ v[b, g].T - oracle.row_dot(do[b, h], O)[:, None])
+            bv[b, g] += np.abs(P).T @ np.abs(do[b, h])
+            bk[b, g] += abs(scale) * np.abs(dS).T @ np.abs(q[b, h])
+            bq[b, h] = abs(scale) * np.abs(dS) @ np.abs(k[b, g])
+    return U_BF16 * bq, U_BF16 * bk, U_BF16 * bv
+
+
+def run_fwd_bwd(inp, scale, causal, grad_f32=True):
+    import torch
+    q, k, v, do = upload(inp)
+    o, lse = binding.forward(q, k, v, scale, causal, out_dtype=torch.float32)
+    dq, dk, dv, dvec = binding.backward(q, k, v, o, lse, do, scale, causal,
+                                        grad_dtype=torch.float32 if grad_f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    return host(o), host(lse), host(dq), host(dk), host(dv), host(dvec)
+
+
+CASES = [
+    # (B, Hq, Hkv, Nq, Nk, d, causal)
+    (1, 1, 1, 1, 1, 128, True),
+    (1, 1, 1, 17, 17, 64, True),
+    (1, 2, 2, 127, 127, 128, True),
+    (1, 2, 1, 129, 129, 128, False),
+    (2, 4, 2, 200, 200, 64, True),
+    (1, 4, 1, 300, 300, 128, True),
+    (1, 2, 2, 100, 257, 128, False),
+    (1, 2, 2, 333, 65, 64, False),
+    (1, 8, 2, 512, 512, 128, True),
+]
+IDS = [f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}" for c in CASES]
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_bwd_parity(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    announce(f"bwd {case}")
+    inp = gen(300 + Nq + d, B, Hq, Hkv, Nq, Nk, d, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L, dQ, dK, dV, Dv = run_fwd_bwd(inp, scale, causal)
+    dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    bq, bk, bv = rounding_bounds(inp, scale, causal)
+    assert np.all(np.abs(dQ - dQr) <= TOL + bq), "dQ"
+    assert np.all(np.abs(dK - dKr) <= TOL + bk), "dK"
+    assert np.all(np.abs(dV - dVr) <= TOL + bv), "dV"
+    # D = rowsum(dO o O) of the O the kernel was given.
+    assert np.max(np.abs(Dv - oracle.row_dot(inp.do, O))) <= 1e-4
+    # Sum rules: sum_j dK_j = 0, sum_j dV_j = group sum of sum_i dO_i.
+    G = Hq // Hkv
+    assert np.max(np.abs(dK.sum(axis=2))) <= 0.05
+    ref = inp.do.astype(np.float64).reshape(B, Hkv, G, Nq, d).sum(axis=(2, 3))
+    assert np.max(np.abs(dV.sum(axis=2) - ref)) <= 0.05 + 1e-3 * np.max(np.abs(ref))
+
+
+def test_bwd_bf16_grads():
+    announce("bwd bf16 grads")
+    inp = gen(41, 1, 4, 2, 300, 300, 128, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, scale, True, grad_f32=False)
+    dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, True)
+    bq, bk, bv = rounding_bounds(inp, scale, True)
+    assert np.all(np.abs(dQ - dQr) <= TOL + bq)
+    assert np.all(np.abs(dK - dKr) <= TOL + bk + bf16_half_ulp(dKr))
+    assert np.all(np.abs(dV - dVr) <= TOL + bv + bf16_half_ulp(dVr))
+
+
+def test_bwd_zero_scale():
+    announce("bwd scale 0")
+    inp = gen(42, 1, 2, 1, 150, 150, 64, with_do=True)
+    for causal in (False, True):
+        _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, 0.0, causal)
+        assert np.all(dQ == 0.0) and np.all(dK == 0.0)
+        _, _, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, 0.0, causal)
+        assert np.max(np.abs(dV - dVr)) <= TOL
