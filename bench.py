@@ -157,7 +157,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the attention path has no multi-GPU mode; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(the attention path runs on one GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

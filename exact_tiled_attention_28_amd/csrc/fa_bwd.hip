@@ -103,25 +103,6 @@ struct BwdTile {
   static_assert(NDQ >= 1, "dQ blocks per wave");
 };
 
-// Transpose read of 4 bf16 down a column: lane (16-lane block b, index i)
-// gets rows row0(g) + e, e = 0..3, of column col0 + i, given that each lane
-// supplies the address of 4 consecutive columns of one row (verified on
-// gfx950: result[i][e] = loaded[4e + i/4][i%4] within each 16-lane block).
-template <int RC>
-__device__ __forceinline__ short4v tr_read(const char* tile, int row_base, int col_base_elems, int lane) {
-  const int j = lane & 15;
-  const int row = row_base + (j >> 2);
-  const int col = col_base_elems + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const char* p = tile + tile_off<RC>(row, col * 2);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(p));
-}
-
-__device__ __forceinline__ bf16x8 cat4(short4v a, short4v b) {
-  typedef __attribute__((ext_vector_type(8))) short short8v;
-  short8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 template <int D, bool CAUSAL, bool GF32>
 __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;

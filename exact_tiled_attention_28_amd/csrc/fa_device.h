@@ -84,4 +84,39 @@ __device__ __forceinline__ int tile_off(int row, int byte_in_row) {
   return row * (ROW_CHUNKS * 16) + (((c ^ swz<ROW_CHUNKS>(row)) << 4) | (byte_in_row & 15));
 }
 
+// Transpose read of 4 bf16 down a column of a swizzled bf16 LDS tile
+// (ds_read_b64_tr_b16). Each lane supplies the address of 4 consecutive
+// columns of one row; within each 16-lane block the hardware hands lane i
+// element i%4 of lane 4e + i/4 as its element e (checked on gfx950). With
+// lane j of block b pointing at row row_base + j/4, columns
+// col_base + 16*(b%2) + 4*(j%4), lane i of block b receives rows
+// row_base + e (e = 0..3) of column col_base + 16*(b%2) + i.
+template <int RC>
+__device__ __forceinline__ short4v tr_read(const char* tile, int row_base, int col_base_elems, int lane) {
+  const int j = lane & 15;
+  const int row = row_base + (j >> 2);
+  const int col = col_base_elems + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const char* p = tile + tile_off<RC>(row, col * 2);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(p));
+}
+
+// Two transpose reads joined into one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 cat4(short4v a, short4v b) {
+  typedef __attribute__((ext_vector_type(8))) short short8v;
+  short8v r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// HBM -> LDS without registers (global_load_lds_dwordx4): every lane fetches
+// 16 bytes from its own global address; lane l's bytes land at
+// lds_wave_base + 16*l (checked on gfx950). lds_wave_base must be uniform
+// across the wavefront.
+__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until this wavefront's outstanding vector-memory loads (including the
+// HBM -> LDS ones) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace fa

@@ -45,17 +45,29 @@ struct FwdTile {
   static constexpr int RC = ROWB / 16;       // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;    // bytes per K or V tile
   static constexpr int NT = 64 * NW;         // threads per workgroup
-  static constexpr int CPT = BC * RC / NT;   // chunks per thread per tile
-  static_assert(BC * RC % NT == 0, "tile chunks must split evenly over threads");
+  static constexpr int CPW = TILEB / (1024 * NW);  // HBM->LDS loads per wave per tile
+  static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole wave loads");
 };
 
+// The accumulator is rescaled only on tiles where some row's running max
+// grows; on the other tiles exp(m_old - m_new) = 1 for every row and the
+// multiply is skipped. The reference max is always the exact running max, so
+// the largest probability of a row is exactly 1 (no bf16 rounding on it),
+// as in the eager rescale.
+
 template <bool F32IN, int D, bool CAUSAL, bool OUTF32, int NW>
-__global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(F32IN ? 1 : 2, F32IN ? 1 : 2)))
+fwd_kernel(FwdArgs a) {
   using T = FwdTile<F32IN, D, NW>;
   constexpr int BR = T::BR, BC = T::BC, NKB = T::NKB, ROWB = T::ROWB, RC = T::RC, TILEB = T::TILEB;
-  constexpr int NT = T::NT, CPT = T::CPT;
+  constexpr int CPW = T::CPW;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+  // Two K/V buffers as separate objects so that the compiler can tell that
+  // the prefetch into one never aliases the reads of the other.
+  __shared__ __attribute__((aligned(16))) char sK0[TILEB];
+  __shared__ __attribute__((aligned(16))) char sV0[TILEB];
+  __shared__ __attribute__((aligned(16))) char sK1[TILEB];
+  __shared__ __attribute__((aligned(16))) char sV1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,156 +122,174 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
   const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
-  // ---- K/V tile staging: HBM -> registers -> swizzled LDS -----------------
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int jt) {
+  // ---- K/V tile staging: HBM -> swizzled LDS, no registers ------------------
+  // Wave w fills chunks [64*(w*CPW+u), +64) of each tile; chunk p of row r
+  // holds logical chunk p ^ swz(r). Rows past the end of K/V repeat the last
+  // row (their scores are masked).
+  auto issue_tile = [&](int jt, char* Kt, char* Vt) {
     const int kv0 = jt * BC;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / RC, c = ci % RC;
-      if (kv0 + row < a.Nk) {
-        const size_t off = (size_t)(kv0 + row) * ROWB + c * 16;
-        kr[u] = *(const u32x4*)(Kh + off);
-        vr[u] = *(const u32x4*)(Vh + off);
-      } else {
-        kr[u] = u32x4{0u, 0u, 0u, 0u};
-        vr[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* Kt = smem + buf * 2 * TILEB;
-    char* Vt = Kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / RC, c = ci % RC;
-      const int off = tile_off<RC>(row, c * 16);
-      *(u32x4*)(Kt + off) = kr[u];
-      *(u32x4*)(Vt + off) = vr[u];
+    for (int u = 0; u < CPW; ++u) {
+      const int cb = (w * CPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / RC, pc = idx % RC;
+      const int lc = pc ^ swz<RC>(row);
+      const int grow = min(kv0 + row, a.Nk - 1);
+      const size_t off = (size_t)grow * ROWB + lc * 16;
+      load_lds_16(Kh + off, Kt + cb * 16);
+      load_lds_16(Vh + off, Vt + cb * 16);
     }
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY;  // running max, log2 units (scaled scores)
+  float m = -INFINITY;  // reference max, log2 units (scaled scores)
   float lsum = 0.0f;    // running sum over this half-wave's keys
   const float c = a.c;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Per-lane LDS byte offsets of the MFMA operand fetches, computed once.
+  // The swizzle of a row depends only on the row modulo 16 (modulo 32 for
+  // 8-chunk rows), so moving by whole 32-key blocks or 16-key steps adds a
+  // constant that folds into the instruction's immediate offset.
+  constexpr int NKOFF = F32IN ? 1 : NQF;
+  int koff[NKOFF];
+  int voff[F32IN ? 1 : D / 32][2];
+  if constexpr (!F32IN) {
+#pragma unroll
+    for (int kk = 0; kk < NQF; ++kk) koff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
+    const int j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        voff[db][h] = tile_off<RC>(4 * g + 8 * h + (j >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2);
+  }
 
-  for (int jt = 0; jt < n_kv; ++jt) {
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
-    const bool has_next = jt + 1 < n_kv;
-    if (has_next) load_tile(jt + 1);
-    const char* Kt = smem + (jt & 1) * 2 * TILEB;
-    const char* Vt = Kt + TILEB;
-
-    // A wavefront whose 32 rows all lie above this tile skips it.
-    const bool active = !CAUSAL || kv0 <= q0w + 31;
-    if (active) {
-      // ---- S^T = K_j Q_i^T ------------------------------------------------
-      f32x16 sacc[NKB];
+    // ---- S^T = K_j Q_i^T ------------------------------------------------------
+    f32x16 sacc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = f32x16{};
-        const int krow = kb * 32 + l32;
-        if constexpr (F32IN) {
-#pragma unroll
-          for (int kk = 0; kk < NQF; ++kk) {
-            const float ka = *(const float*)(Kt + tile_off<RC>(krow, (2 * kk + g) * 4));
-            sacc[kb] = mfma_f32(ka, qf[kk], sacc[kb]);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < NQF; ++kk) {
-            const bf16x8 ka = *(const bf16x8*)(Kt + tile_off<RC>(krow, (kk * 16 + 8 * g) * 2));
-            sacc[kb] = mfma_bf16(ka, qf[kk], sacc[kb]);
-          }
-        }
-      }
-
-      // ---- mask (diagonal-crossing or ragged tiles only) --------------------
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
-            sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
-          }
-      }
-
-      // ---- online softmax ---------------------------------------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m, mx * c);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[kb][r], c, -m_new));
-          if (need_mask) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
-          sacc[kb][r] = p;
-          rs += p;
-        }
-      lsum = fmaf(alpha, lsum, rs);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-
-      // ---- O^T += V_j^T P^T -------------------------------------------------
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
       if constexpr (F32IN) {
+        const int krow = kb * 32 + l32;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const float va = *(const float*)(Vt + tile_off<RC>(key, (db * 32 + l32) * 4));
-              oacc[db] = mfma_f32(va, sacc[kb][r], oacc[db]);
-            }
-          }
+        for (int kk = 0; kk < NQF; ++kk) {
+          const float ka = *(const float*)(Kt + tile_off<RC>(krow, (2 * kk + g) * 4));
+          sacc[kb] = mfma_f32(ka, qf[kk], sacc[kb]);
+        }
       } else {
-        // Step t covers keys 16t..16t+15; slot (g, v) of both operands holds
-        // key 16t + 8*(v/4) + 4g + v%4, which is where the S^T accumulator
-        // registers 8*(t%2)..8*(t%2)+7 of block t/2 put it.
 #pragma unroll
-        for (int t = 0; t < BC / 16; ++t) {
-          float pv[8];
-#pragma unroll
-          for (int v = 0; v < 8; ++v) pv[v] = sacc[t >> 1][8 * (t & 1) + v];
-          const bf16x8 pb = to_bf16x8(pv);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            bf16x8 va;
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-              const int key = 16 * t + 8 * (v >> 2) + 4 * g + (v & 3);
-              va[v] = *(const __bf16*)(Vt + tile_off<RC>(key, (db * 32 + l32) * 2));
-            }
-            oacc[db] = mfma_bf16(va, pb, oacc[db]);
-          }
+        for (int kk = 0; kk < NQF; ++kk) {
+          const bf16x8 ka = *(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB);
+          sacc[kb] = mfma_bf16(ka, qf[kk], sacc[kb]);
         }
       }
     }
 
-    if (has_next) store_tile((jt + 1) & 1);
+    // ---- mask (diagonal-crossing or ragged tiles only) ------------------------
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
+          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+        }
+    }
+
+    // ---- online softmax ---------------------------------------------------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    const float mxs = half_swap_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mxs > m) != 0) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
+        if constexpr (MASK) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
+        sacc[kb][r] = p;
+        rs += p;
+      }
+    lsum += rs;
+
+    // ---- O^T += V_j^T P^T ---------------------------------------------------------
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const float va = *(const float*)(Vt + tile_off<RC>(key, (db * 32 + l32) * 4));
+            oacc[db] = mfma_f32(va, sacc[kb][r], oacc[db]);
+          }
+        }
+    } else {
+      // Step t covers keys 16t..16t+15; slot (g, v) of both operands holds
+      // key 16t + 8*(v/4) + 4g + v%4, which is where the S^T accumulator
+      // registers 8*(t%2)..8*(t%2)+7 of block t/2 put it; the V^T operand is
+      // read down the key column with two transpose reads.
+#pragma unroll
+      for (int t = 0; t < BC / 16; ++t) {
+        float pv[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) pv[v] = sacc[t >> 1][8 * (t & 1) + v];
+        const bf16x8 pb = to_bf16x8(pv);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const char* vp = Vt + 16 * t * ROWB;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][0]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][1]));
+          oacc[db] = mfma_bf16(cat4(lo, hi), pb, oacc[db]);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) {
+    const int kv0 = jt * BC;
+    if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
+    // A wavefront whose 32 rows all lie above this tile skips it; tiles that
+    // cross the diagonal or the end of K/V take the masked body.
+    const bool active = !CAUSAL || kv0 <= q0w + 31;
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
+    if (active) {
+      if (need_mask)
+        body(std::true_type{}, jt, Kt, Vt);
+      else
+        body(std::false_type{}, jt, Kt, Vt);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  issue_tile(0, sK0, sV0);
+  wait_vmem();
+  __syncthreads();
+  int jt = 0;
+  for (; jt + 1 < n_kv; jt += 2) {
+    step(jt, sK0, sV0, sK1, sV1);
+    step(jt + 1, sK1, sV1, sK0, sV0);
   }
+  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
 
   // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
   const float lt = half_swap_add(lsum);
