@@ -80,7 +80,7 @@ struct BwdTile {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;  // keys per workgroup (32 per wavefront)
   static constexpr int BQ = 64;        // query rows per step
-  static constexpr int QROWB = D * 2;  // bytes per Q / dO row
+  static constexpr int QROWB = D * 2;  // bytes per Q / dO / K row
   static constexpr int QRC = QROWB / 16;
   static constexpr int QTILEB = BQ * QROWB;
   static constexpr int KTILEB = BKV * QROWB;
@@ -88,28 +88,28 @@ struct BwdTile {
   static constexpr int SRC = SROWB / 16;
   static constexpr int STILEB = BKV * SROWB;
   static constexpr int NT = 64 * NW;
-  static constexpr int QCPT = BQ * QRC / NT;  // Q (and dO) chunks per thread
+  static constexpr int QCPW = QTILEB / (1024 * NW);  // HBM->LDS loads per wave per Q (or dO) tile
   static constexpr int KCPT = BKV * QRC / NT;
-  static constexpr int NDQ = (BQ / 32) * (D / 32) / NW;  // dQ 32x32 blocks per wave
+  static constexpr int NDB = D / 32;                 // 32-column blocks of the head dim
+  static constexpr int NDQ = (BQ / 32) * NDB / NW;   // dQ 32x32 blocks per wave
   // LDS carve-up (bytes)
-  static constexpr int OFF_Q = 0;                         // [2][QTILEB]
-  static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;       // [2][QTILEB]
-  static constexpr int OFF_K = OFF_DO + 2 * QTILEB;       // [KTILEB]
-  static constexpr int OFF_S = OFF_K + KTILEB;            // [STILEB]
-  static constexpr int OFF_L = OFF_S + STILEB;            // [2][BQ] fp32 (L * log2 e)
-  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;        // [2][BQ] fp32
+  static constexpr int OFF_Q = 0;                    // [2][QTILEB]
+  static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;  // [2][QTILEB]
+  static constexpr int OFF_K = OFF_DO + 2 * QTILEB;  // [KTILEB]
+  static constexpr int OFF_S = OFF_K + KTILEB;       // [STILEB]
+  static constexpr int OFF_L = OFF_S + STILEB;       // [2][BQ] fp32 (L * log2 e)
+  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;   // [2][BQ] fp32
   static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
-  static_assert(BQ * QRC % NT == 0 && BKV * QRC % NT == 0, "tiles must split evenly");
-  static_assert(NDQ >= 1, "dQ blocks per wave");
+  static_assert(QTILEB % (1024 * NW) == 0 && BKV * QRC % NT == 0, "tiles must split evenly");
+  static_assert((BQ / 32) * NDB % NW == 0 && NDQ >= 1, "dQ blocks must split evenly over waves");
 };
 
 template <int D, bool CAUSAL, bool GF32>
 __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
   constexpr int BKV = T::BKV, BQ = T::BQ, QROWB = T::QROWB, QRC = T::QRC, QTILEB = T::QTILEB, SRC = T::SRC;
-  constexpr int NT = T::NT, QCPT = T::QCPT, KCPT = T::KCPT, NDQ = T::NDQ;
+  constexpr int NT = T::NT, QCPW = T::QCPW, KCPT = T::KCPT, NDQ = T::NDQ, NDB = T::NDB;
   constexpr int NKK = D / 16;  // K-steps of the S / dP products
-  constexpr int NDB = D / 32;  // 32-column blocks of the head dim
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const sQ = smem + T::OFF_Q;
@@ -124,6 +124,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const int w = tid >> 6;
   const int g = lane >> 5;
   const int l32 = lane & 31;
+  const int j16 = lane & 15;
 
   // Work decode: (batch, kv head) fastest, K/V blocks from the first (the
   // heaviest under the causal mask) to the last.
@@ -156,11 +157,30 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int u = 0; u < KCPT; ++u) {
     const int ci = tid + NT * u;
-    const int row = ci / QRC, c = ci % QRC;
+    const int row = ci / QRC, cc = ci % QRC;
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (kv0 + row < a.Nk) x = *(const u32x4*)(Kh + (size_t)(kv0 + row) * QROWB + c * 16);
-    *(u32x4*)(sK + tile_off<QRC>(row, c * 16)) = x;
+    if (kv0 + row < a.Nk) x = *(const u32x4*)(Kh + (size_t)(kv0 + row) * QROWB + cc * 16);
+    *(u32x4*)(sK + tile_off<QRC>(row, cc * 16)) = x;
   }
+
+  // Per-lane LDS byte offsets, computed once. Row swizzles repeat every 16
+  // rows (32 for 8-chunk rows), so whole 32-row blocks and 16-row steps only
+  // add constants.
+  int qoff[NKK];  // A operand rows of Q / dO: row l32, head-dim step kk
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qoff[kk] = tile_off<QRC>(l32, (kk * 16 + 8 * g) * 2);
+  int troff[NDB][2];  // transpose reads of Q / dO / K: column block db, half h
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      troff[db][h] = tile_off<QRC>(4 * g + 8 * h + (j16 >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
+  int tsoff[BQ / 32][2];  // transpose reads of dS^T: query block qb, half h
+#pragma unroll
+  for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      tsoff[qb][h] = tile_off<SRC>(4 * g + 8 * h + (j16 >> 2), (qb * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -176,10 +196,10 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const float c = a.c;
   const float scale = a.scale;
 
-  // ---- Q_i / dO_i / L_i / D_i staging --------------------------------------
-  u32x4 qr[QCPT], dor[QCPT];
+  // ---- Q_i / dO_i tiles: HBM -> swizzled LDS without registers; L_i, D_i
+  // through registers (rows past the end get L = +inf, so P = 0 there) ----
   float lr = 0.0f, dr = 0.0f;
-  auto load_q = [&](int it) {
+  auto issue_q = [&](int it, int buf) {
     const int hm = it / n_i;
     const int i = i_first + it % n_i;
     const int hq = hkv * a.G + hm;
@@ -188,34 +208,22 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     const char* Qh = (const char*)a.q + qhead * QROWB;
     const char* Oh = (const char*)a.dout + qhead * QROWB;
 #pragma unroll
-    for (int u = 0; u < QCPT; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / QRC, cc = ci % QRC;
-      if (q0 + row < a.Nq) {
-        const size_t off = (size_t)(q0 + row) * QROWB + cc * 16;
-        qr[u] = *(const u32x4*)(Qh + off);
-        dor[u] = *(const u32x4*)(Oh + off);
-      } else {
-        qr[u] = u32x4{0u, 0u, 0u, 0u};
-        dor[u] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int u = 0; u < QCPW; ++u) {
+      const int cb = (w * QCPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / QRC, pc = idx % QRC;
+      const int lc = pc ^ swz<QRC>(row);
+      const size_t off = (size_t)min(q0 + row, a.Nq - 1) * QROWB + lc * 16;
+      load_lds_16(Qh + off, sQ + buf * QTILEB + cb * 16);
+      load_lds_16(Oh + off, sDO + buf * QTILEB + cb * 16);
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < a.Nq;
-      // Rows past the end get L = +inf, so P = exp2(S c - inf) = 0 there.
       lr = ok ? a.lse[qhead + q0 + tid] * kLog2e : INFINITY;
       dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
     }
   };
-  auto store_q = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < QCPT; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / QRC, cc = ci % QRC;
-      const int off = tile_off<QRC>(row, cc * 16);
-      *(u32x4*)(sQ + buf * QTILEB + off) = qr[u];
-      *(u32x4*)(sDO + buf * QTILEB + off) = dor[u];
-    }
+  auto store_ld = [&](int buf) {
     if (tid < BQ) {
       sL[buf * BQ + tid] = lr;
       sD[buf * BQ + tid] = dr;
@@ -223,9 +231,10 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   };
 
   if (total > 0) {
-    load_q(0);
-    store_q(0);
+    issue_q(0, 0);
+    store_ld(0);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
@@ -236,7 +245,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
     const int q0 = i * BQ;
     const bool has_next = it + 1 < total;
-    if (has_next) load_q(it + 1);
+    if (has_next) issue_q(it + 1, buf ^ 1);
 
     const char* tQ = sQ + buf * QTILEB;
     const char* tDO = sDO + buf * QTILEB;
@@ -246,24 +255,18 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     // A wavefront whose keys all lie after every query of this block skips
     // the products; its dS^T rows are written as zeros.
     const bool active = !CAUSAL || kv0 + 32 * w <= q0 + BQ - 1;
-    f32x16 ds[BQ / 32];
+    bf16x8 dsb[BQ / 16];
     if (active) {
-      // ---- S = Q_i K_j^T and dP = dO_i V_j^T (one key per lane) -----------
-      f32x16 s[BQ / 32], dp[BQ / 32];
+      // ---- S = Q_i K_j^T (one key per lane, query rows in registers) -------
+      f32x16 s[BQ / 32];
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
         s[qb] = f32x16{};
-        dp[qb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int off = tile_off<QRC>(qb * 32 + l32, (kk * 16 + 8 * g) * 2);
-          const bf16x8 qa = *(const bf16x8*)(tQ + off);
-          const bf16x8 oa = *(const bf16x8*)(tDO + off);
-          s[qb] = mfma_bf16(qa, kf[kk], s[qb]);
-          dp[qb] = mfma_bf16(oa, vf[kk], dp[qb]);
-        }
+        for (int kk = 0; kk < NKK; ++kk)
+          s[qb] = mfma_bf16(*(const bf16x8*)(tQ + qoff[kk] + qb * 32 * QROWB), kf[kk], s[qb]);
       }
-      // ---- P = exp2(S c - L log2 e), dS = P o (dP - D) ----------------------
+      // ---- P = exp2(S c - L log2 e) --------------------------------------------
       const bool need_mask = (CAUSAL && kv0 + 32 * w + 31 > q0) || (kv0 + 32 * w + 32 > a.Nk);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb)
@@ -271,69 +274,91 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
         for (int a4 = 0; a4 < 4; ++a4) {
           const int r0 = qb * 32 + 8 * a4 + 4 * g;
           const f32x4 lv = *(const f32x4*)(tL + r0);
-          const f32x4 dv = *(const f32x4*)(tD + r0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a4 + e;
-            float p = fast_exp2(fmaf(s[qb][r], c, -lv[e]));
+            float p = fast_exp2(fmaf(s[qb][4 * a4 + e], c, -lv[e]));
             if (need_mask) {
               const bool vis = key < a.Nk && (!CAUSAL || key <= q0 + r0 + e);
               p = vis ? p : 0.0f;
             }
-            s[qb][r] = p;
-            ds[qb][r] = p * (dp[qb][r] - dv[e]);
+            s[qb][4 * a4 + e] = p;
           }
         }
-      // ---- dV^T += dO_i^T P and dK^T += Q_i^T dS -----------------------------
+      // ---- dV^T += dO_i^T P ------------------------------------------------------
 #pragma unroll
       for (int t = 0; t < BQ / 16; ++t) {
-        float pv[8], sv[8];
+        float pv[8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          pv[v] = s[t >> 1][8 * (t & 1) + v];
-          sv[v] = ds[t >> 1][8 * (t & 1) + v];
-        }
+        for (int v = 0; v < 8; ++v) pv[v] = s[t >> 1][8 * (t & 1) + v];
         const bf16x8 pb = to_bf16x8(pv);
-        const bf16x8 sb = to_bf16x8(sv);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int rb = 16 * t + 4 * ((lane >> 5) & 1);
-          const bf16x8 doa = cat4(tr_read<QRC>(tDO, rb, db * 32, lane), tr_read<QRC>(tDO, rb + 8, db * 32, lane));
-          const bf16x8 qa = cat4(tr_read<QRC>(tQ, rb, db * 32, lane), tr_read<QRC>(tQ, rb + 8, db * 32, lane));
-          dvacc[db] = mfma_bf16(doa, pb, dvacc[db]);
-          dkacc[db] = mfma_bf16(qa, sb, dkacc[db]);
+          const char* base = tDO + 16 * t * QROWB;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+          dvacc[db] = mfma_bf16(cat4(lo, hi), pb, dvacc[db]);
         }
       }
+      // ---- dP = dO_i V_j^T, dS = P o (dP - D) -----------------------------------
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) {
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          dp = mfma_bf16(*(const bf16x8*)(tDO + qoff[kk] + qb * 32 * QROWB), vf[kk], dp);
+        float dsv[16];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 dv = *(const f32x4*)(tD + qb * 32 + 8 * a4 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dsv[4 * a4 + e] = s[qb][4 * a4 + e] * (dp[4 * a4 + e] - dv[e]);
+        }
+        dsb[2 * qb] = to_bf16x8(dsv);
+        dsb[2 * qb + 1] = to_bf16x8(dsv + 8);
+      }
+      // ---- dK^T += Q_i^T dS --------------------------------------------------------
+#pragma unroll
+      for (int t = 0; t < BQ / 16; ++t)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const char* base = tQ + 16 * t * QROWB;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+          dkacc[db] = mfma_bf16(cat4(lo, hi), dsb[t], dkacc[db]);
+        }
     } else {
 #pragma unroll
-      for (int qb = 0; qb < BQ / 32; ++qb) ds[qb] = f32x16{};
+      for (int t = 0; t < BQ / 16; ++t) dsb[t] = bf16x8{};
     }
 
-    // ---- stage dS^T (keys x queries, bf16) ----------------------------------
+    // ---- stage dS^T (keys x queries, bf16): register 4*a4+e of block qb
+    // holds query qb*32 + 8*a4 + 4g + e -----------------------------------------
 #pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb)
+    for (int t = 0; t < BQ / 16; ++t)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 x = {ds[qb][4 * a4], ds[qb][4 * a4 + 1], ds[qb][4 * a4 + 2], ds[qb][4 * a4 + 3]};
-        const int col = qb * 32 + 8 * a4 + 4 * g;
-        *(bf16x4*)(sS + tile_off<SRC>(key_l, col * 2)) = __builtin_convertvector(x, bf16x4);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = (t >> 1) * 32 + 8 * (2 * (t & 1) + hh) + 4 * g;
+        const bf16x4 v4 = {dsb[t][4 * hh], dsb[t][4 * hh + 1], dsb[t][4 * hh + 2], dsb[t][4 * hh + 3]};
+        *(bf16x4*)(sS + tile_off<SRC>(key_l, col * 2)) = v4;
       }
     __syncthreads();
 
-    // ---- dQ_i += scale * dS K_j (fp32 atomics) ------------------------------
+    // ---- dQ_i += scale * dS K_j (fp32 atomics) --------------------------------
 #pragma unroll
     for (int u = 0; u < NDQ; ++u) {
       const int bi = w + T::NW * u;
       const int qb = bi / NDB, db = bi % NDB;
-      f32x16 acc = f32x16{};
-      const bool any = !CAUSAL || q0 + qb * 32 + 31 >= kv0;
-      if (any) {
+      if (!CAUSAL || q0 + qb * 32 + 31 >= kv0) {
+        f32x16 acc = f32x16{};
 #pragma unroll
         for (int t = 0; t < BKV / 16; ++t) {
-          const int rb = 16 * t + 4 * ((lane >> 5) & 1);
-          const bf16x8 sa = cat4(tr_read<SRC>(sS, rb, qb * 32, lane), tr_read<SRC>(sS, rb + 8, qb * 32, lane));
-          const bf16x8 kb = cat4(tr_read<QRC>(sK, rb, db * 32, lane), tr_read<QRC>(sK, rb + 8, db * 32, lane));
-          acc = mfma_bf16(sa, kb, acc);
+          const char* sb = sS + 16 * t * T::SROWB;
+          const char* kb = sK + 16 * t * QROWB;
+          const short4v slo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][0]));
+          const short4v shi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][1]));
+          const short4v klo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][0]));
+          const short4v khi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][1]));
+          acc = mfma_bf16(cat4(slo, shi), cat4(klo, khi), acc);
         }
         float* dqh = a.dq + qhead * D;
 #pragma unroll
@@ -344,7 +369,8 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
       }
     }
 
-    if (has_next) store_q(buf ^ 1);
+    if (has_next) store_ld(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
