@@ -1,0 +1,196 @@
+"""CPU tests of the C-ABI library: it loads, exports every function that
+include/fa.h declares, reports every argument error on the host before any
+launch, and its tile bookkeeping header matches a brute-force mask. No test
+here runs a kernel."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from exact_tiled_attention_28_amd import binding
+from exact_tiled_attention_28_amd import build as fa_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        fa_build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[a-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(
+        ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_last_error", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "fa.h"\nint main(void) { return fa_version() == 1 ? 0 : 1; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", f"-I{os.path.join(ROOT, 'include')}",
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_misc_entry_points(lib):
+    assert binding.fa_version() == 1
+    assert binding.fa_status_string(0) == "FA_OK"
+    assert binding.fa_status_string(1) == "FA_ERR_INVALID_ARGUMENT"
+    assert binding.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert binding.fa_status_string(3) == "FA_ERR_HIP"
+    assert binding.fa_status_string(99) == "FA_ERR_UNKNOWN"
+    assert binding.fa_bwd_workspace_bytes(2, 3, 5) == 4 * 2 * 3 * 5
+    assert binding.fa_bwd_workspace_bytes(0, 3, 5) == 0
+    assert binding.fa_bwd_workspace_bytes(-1, 3, 5) == 0
+
+
+# Fake, aligned, never-dereferenced "device" addresses: every call below fails
+# validation before anything touches them.
+P = 0x10000
+MIS = 0x10008  # 8-byte aligned, not 16
+
+
+def fwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, batch=1, n_q_heads=2, n_kv_heads=1, seqlen_q=16, seqlen_k=16,
+                head_dim=64, scale=0.125, causal=0, in_dtype=1, out_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_fwd(*args.values())
+
+
+def bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, batch=1, n_q_heads=2, n_kv_heads=1,
+                seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
+                stream=None)
+    args.update(kw)
+    return binding.fa_bwd(*args.values())
+
+
+INVALID = binding.FA_ERR_INVALID_ARGUMENT
+UNSUP = binding.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(lse=0), INVALID, "lse is NULL"),
+    (dict(v=MIS), INVALID, "v is not 16-byte aligned"),
+    (dict(batch=0), INVALID, "sizes must be >= 1"),
+    (dict(seqlen_k=-3), INVALID, "sizes must be >= 1"),
+    (dict(n_q_heads=3, n_kv_heads=2), INVALID, "multiple of n_kv_heads"),
+    (dict(causal=2), INVALID, "causal must be 0 or 1"),
+    (dict(scale=float("nan")), INVALID, "scale must be finite"),
+    (dict(scale=float("inf")), INVALID, "scale must be finite"),
+    (dict(in_dtype=7), INVALID, "FA_DTYPE"),
+    (dict(out_dtype=-1), INVALID, "FA_DTYPE"),
+    (dict(head_dim=96), UNSUP, "head_dim 96 unsupported"),
+    (dict(causal=1, seqlen_q=16, seqlen_k=17), UNSUP, "seqlen_q == seqlen_k"),
+    (dict(seqlen_q=1 << 25, head_dim=128), INVALID, "below 2^31"),
+])
+def test_fwd_argument_errors(lib, kw, code, text):
+    assert fwd(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dout=0), INVALID, "dout is NULL"),
+    (dict(ws=0), INVALID, "workspace is NULL"),
+    (dict(dq=MIS), INVALID, "dq is not 16-byte aligned"),
+    (dict(n_kv_heads=0), INVALID, "sizes must be >= 1"),
+    (dict(grad_dtype=5), INVALID, "FA_DTYPE"),
+    (dict(in_dtype=0), UNSUP, "bf16"),
+    (dict(head_dim=32), UNSUP, "head_dim 32"),
+    (dict(causal=1, seqlen_k=15), UNSUP, "seqlen_q == seqlen_k"),
+])
+def test_bwd_argument_errors(lib, kw, code, text):
+    assert bwd(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+def test_errors_are_thread_local(lib):
+    import threading
+    assert fwd(q=0) == INVALID
+    seen = {}
+
+    def other():
+        seen["before"] = binding.fa_last_error()
+        fwd(head_dim=48)
+        seen["after"] = binding.fa_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["before"] == ""
+    assert "head_dim 48" in seen["after"]
+    assert binding.fa_last_error() == "q is NULL"
+
+
+TILE_PROBE = r"""
+#include <cstdio>
+#include "fa_tiles.h"
+int main() {
+  for (int q0 = 0; q0 < 40; q0 += 3)
+    for (int nq = 1; nq <= 9; nq += 4)
+      for (int k0 = 0; k0 < 40; k0 += 5)
+        for (int nk = 1; nk <= 9; nk += 4)
+          std::printf("%d %d %d %d %d\n", q0, nq, k0, nk, (int)fa::causal_tile_class(q0, nq, k0, nk));
+  for (int n = 1; n <= 300; n += 7)
+    for (int br = 16; br <= 128; br *= 2)
+      for (int bc = 16; bc <= 128; bc *= 2)
+        for (int q0 = 0; q0 < n; q0 += br)
+          std::printf("K %d %d %d %d %d %d %d\n", n, br, bc, q0, fa::kv_tiles_for(q0, br, n, bc, true),
+                      fa::kv_tiles_for(q0, br, n, bc, false), fa::first_q_tile_for(q0, br, true));
+  return 0;
+}
+"""
+
+
+def test_tile_bookkeeping_matches_brute_force():
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "probe.cpp")
+        exe = os.path.join(tmp, "probe")
+        open(src, "w").write(TILE_PROBE)
+        r = subprocess.run(["g++", "-std=c++17", "-O1", f"-I{os.path.join(ROOT, 'exact_tiled_attention_28_amd', 'csrc')}",
+                            src, "-o", exe], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.splitlines()
+    n_cls = n_trip = 0
+    for ln in lines:
+        f = ln.split()
+        if f[0] == "K":
+            n, br, bc, q0, trips_c, trips_n, first = map(int, f[1:])
+            rows = range(q0, min(n, q0 + br))
+            # brute force: the last key any row of the tile may see (key <= row)
+            last_c = max(rows)
+            assert trips_c == (min(n, q0 + br) + bc - 1) // bc and trips_c * bc > last_c
+            assert trips_n == (n + bc - 1) // bc
+            # first Q tile of height br that sees key k0 = q0 (k0 is a multiple of br here)
+            assert first == q0 // br
+            n_trip += 1
+            continue
+        q0, nq, k0, nk, cls = map(int, f)
+        vis = np.array([[c <= r for c in range(k0, k0 + nk)] for r in range(q0, q0 + nq)])
+        expect = 0 if vis.all() else (2 if not vis.any() else 1)
+        assert cls == expect, (q0, nq, k0, nk)
+        n_cls += 1
+    assert n_cls > 500 and n_trip > 500
