@@ -2,8 +2,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-fa_fwd (bf16 O, fp32 L) followed by fa_bwd (D preprocess + main kernel,
-fp32 dQ, bf16 dK/dV) on the causal bf16 workload B=8, H=16, N=2048, d=128
+fa_fwd (bf16 O, fp32 L) followed by fa_bwd (D preprocess, dK/dV kernel,
+dQ kernel; fp32 dQ, bf16 dK/dV) on the causal bf16 workload B=8, H=16, N=2048, d=128
 (seed 2), inputs resident in HBM. Prints ONE JSON line.
 
 value = causal-adjusted TFLOPS of the step: forward 4*B*H*N^2*d/2 plus
@@ -96,15 +96,19 @@ class Step:
         if rc:
             raise binding.FAError(rc, "fa_fwd", binding.fa_last_error())
 
-    def bwd(self):
+    def bwd_atomic(self):
+        self.bwd(binding.fa_bwd_atomic)
+
+    def bwd(self, fn=None):
         w = self.w
-        rc = binding.fa_bwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+        fn = fn or binding.fa_bwd
+        rc = fn(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
                             self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
                             self.dv.data_ptr(), self.ws.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen,
                             w.seqlen, w.head_dim, w.scale, int(w.causal), self.code, self.code, self.code,
                             self.sh)
         if rc:
-            raise binding.FAError(rc, "fa_bwd", binding.fa_last_error())
+            raise binding.FAError(rc, fn.__name__, binding.fa_last_error())
 
 
 def time_calls(step, calls, steps, warmup):
@@ -174,6 +178,8 @@ def main():
         raise RuntimeError("dO missing")
     step = Step(w, q, k, v, do)
     per_step, per_call, wall = time_calls(step, [step.fwd, step.bwd], args.steps, args.warmup)
+    _, per_call_atomic, _ = time_calls(step, [step.bwd_atomic], args.steps, args.warmup)
+    ms_bwd_atomic = float(np.median(per_call_atomic[:, 0]))
     ms_step = float(np.median(per_step))
     ms_fwd = float(np.median(per_call[:, 0]))
     ms_bwd = float(np.median(per_call[:, 1]))
@@ -185,7 +191,8 @@ def main():
     avg_fwd = float(np.mean(per_call[:, 0]))
     avg_bwd = float(np.mean(per_call[:, 1]))
     if avg_bwd >= avg_fwd:
-        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_kernel, one call)", "flops": bf, "ms": avg_bwd}
+        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_kernel + bwd_dq_kernel, one call)", "flops": bf,
+               "ms": avg_bwd}
     else:
         dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd}
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
@@ -214,6 +221,9 @@ def main():
                 "pct_of_bf16_peak": round(100 * bwd_tf / MI355X_BF16_PEAK_TFLOPS, 2),
                 "gbps_algorithmic": round(bwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
                                                     w.head_dim) / (ms_bwd * 1e-3) / 1e9, 1)},
+        "bwd_atomic_dq": {"ms": round(ms_bwd_atomic, 4),
+                          "tflops": round(bf / (ms_bwd_atomic * 1e-3) / 1e12, 2),
+                          "note": "fa_bwd_atomic: single pass, dQ by fp32 atomics (not in the timed step)"},
         "wall_ms_per_step": round(wall, 4),
         "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     FAError,
     backward,
     fa_bwd,
+    fa_bwd_atomic,
     fa_bwd_workspace_bytes,
     fa_fwd,
     fa_last_error,

@@ -54,8 +54,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     lib.fa_fwd.restype = _c_int
     lib.fa_fwd.argtypes = [_c_ptr] * 5 + [_c_int] * 6 + [_c_float] + [_c_int] * 3 + [_c_ptr]
-    lib.fa_bwd.restype = _c_int
-    lib.fa_bwd.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    for fn in (lib.fa_bwd, lib.fa_bwd_atomic):
+        fn.restype = _c_int
+        fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -83,6 +84,13 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
                                  seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
                                  stream)
+
+
+def fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+                  head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream) -> int:
+    return load_library().fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
+                                        seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
+                                        stream)
 
 
 def fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q) -> int:
@@ -152,9 +160,10 @@ def forward(q, k, v, scale, causal, out_dtype=None, o=None, lse=None, stream=Non
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None):
+def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None, atomic_dq=False):
     """dQ (fp32), dK, dV (grad_dtype, default the input dtype) and the
-    workspace holding D. Returns (dq, dk, dv, dvec)."""
+    workspace holding D. Returns (dq, dk, dv, dvec). atomic_dq selects
+    fa_bwd_atomic instead of fa_bwd."""
     import torch
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -166,8 +175,9 @@ def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None):
     for t in (q, k, v, o, lse, do):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
-                int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
-    _check(rc, "fa_bwd")
+    fn = fa_bwd_atomic if atomic_dq else fa_bwd
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+            int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
+    _check(rc, fn.__name__)
     return dq, dk, dv, ws[:B * Hq * Nq].view(B, Hq, Nq)

@@ -50,10 +50,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(e, "fa_fwd launch");
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-           float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
-           int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
-           void* stream) {
+}  // extern "C"
+
+static int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads,
+                      int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                      int in_dtype, int o_dtype, int grad_dtype, void* stream, bool atomic_dq, const char* name) {
   std::string err;
   const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
   if (int rc = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, s, scale, causal, in_dtype, o_dtype,
@@ -79,8 +81,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_bwd(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
-                                (hipStream_t)stream);
-  return hip_status(e, "fa_bwd launch");
+                                atomic_dq, (hipStream_t)stream);
+  return hip_status(e, name);
+}
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
+           int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
+           void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream, false, "fa_bwd launch");
+}
+
+int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads,
+                  int seqlen_q, int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype,
+                  int grad_dtype, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream, true, "fa_bwd_atomic launch");
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q) {

@@ -34,10 +34,10 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// preprocess: D = rowsum(dO o O), dQ = 0
+// preprocess: D = rowsum(dO o O), and dQ = 0 when dQ is accumulated atomically
 // ---------------------------------------------------------------------------
 
-template <int D, bool OF32>
+template <int D, bool OF32, bool ZERO_DQ>
 __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const __bf16* __restrict__ dout, const void* __restrict__ o,
                                                              float* __restrict__ dvec, float* __restrict__ dq,
                                                              long long rows) {
@@ -62,9 +62,11 @@ __global__ void __launch_bounds__(256) bwd_preprocess_kernel(const __bf16* __res
     const f32x8 df = __builtin_convertvector(db, f32x8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(df[e], of[e], acc);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(dq + base) = z;
-    *(f32x4*)(dq + base + 4) = z;
+    if constexpr (ZERO_DQ) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(dq + base) = z;
+      *(f32x4*)(dq + base + 4) = z;
+    }
   }
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
@@ -92,19 +94,23 @@ struct BwdTile {
   static constexpr int KCPT = BKV * QRC / NT;
   static constexpr int NDB = D / 32;                 // 32-column blocks of the head dim
   static constexpr int NDQ = (BQ / 32) * NDB / NW;   // dQ 32x32 blocks per wave
-  // LDS carve-up (bytes)
+  // LDS carve-up (bytes); the K tile and dS^T are only needed for atomic dQ
   static constexpr int OFF_Q = 0;                    // [2][QTILEB]
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;  // [2][QTILEB]
-  static constexpr int OFF_K = OFF_DO + 2 * QTILEB;  // [KTILEB]
-  static constexpr int OFF_S = OFF_K + KTILEB;       // [STILEB]
-  static constexpr int OFF_L = OFF_S + STILEB;       // [2][BQ] fp32 (L * log2 e)
+  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;  // [2][BQ] fp32 (L * log2 e)
   static constexpr int OFF_D = OFF_L + 2 * BQ * 4;   // [2][BQ] fp32
-  static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
+  static constexpr int OFF_K = OFF_D + 2 * BQ * 4;   // [KTILEB]
+  static constexpr int OFF_S = OFF_K + KTILEB;       // [STILEB]
+  static constexpr int LDS_BYTES_ATOMIC = OFF_S + STILEB;
+  static constexpr int LDS_BYTES_SPLIT = OFF_K;
   static_assert(QTILEB % (1024 * NW) == 0 && BKV * QRC % NT == 0, "tiles must split evenly");
   static_assert((BQ / 32) * NDB % NW == 0 && NDQ >= 1, "dQ blocks must split evenly over waves");
 };
 
-template <int D, bool CAUSAL, bool GF32>
+// ATOMIC_DQ: also compute dQ_i += scale * dS K_j and add it to the fp32 dQ in
+// HBM with atomics (the fused single-pass scheme). Without it the kernel
+// produces dK and dV only and dQ comes from bwd_dq_kernel (second pass).
+template <int D, bool CAUSAL, bool GF32, bool ATOMIC_DQ>
 __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
   constexpr int BKV = T::BKV, BQ = T::BQ, QROWB = T::QROWB, QRC = T::QRC, QTILEB = T::QTILEB, SRC = T::SRC;
@@ -154,13 +160,15 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     vf[kk] = __builtin_bit_cast(bf16x8, y);
   }
   // K_j tile in LDS for the dQ product.
+  if constexpr (ATOMIC_DQ) {
 #pragma unroll
-  for (int u = 0; u < KCPT; ++u) {
-    const int ci = tid + NT * u;
-    const int row = ci / QRC, cc = ci % QRC;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (kv0 + row < a.Nk) x = *(const u32x4*)(Kh + (size_t)(kv0 + row) * QROWB + cc * 16);
-    *(u32x4*)(sK + tile_off<QRC>(row, cc * 16)) = x;
+    for (int u = 0; u < KCPT; ++u) {
+      const int ci = tid + NT * u;
+      const int row = ci / QRC, cc = ci % QRC;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (kv0 + row < a.Nk) x = *(const u32x4*)(Kh + (size_t)(kv0 + row) * QROWB + cc * 16);
+      *(u32x4*)(sK + tile_off<QRC>(row, cc * 16)) = x;
+    }
   }
 
   // Per-lane LDS byte offsets, computed once. Row swizzles repeat every 16
@@ -331,40 +339,42 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
       for (int t = 0; t < BQ / 16; ++t) dsb[t] = bf16x8{};
     }
 
-    // ---- stage dS^T (keys x queries, bf16): register 4*a4+e of block qb
-    // holds query qb*32 + 8*a4 + 4g + e -----------------------------------------
+    if constexpr (ATOMIC_DQ) {
+      // ---- stage dS^T (keys x queries, bf16): register 4*a4+e of block qb
+      // holds query qb*32 + 8*a4 + 4g + e -----------------------------------------
 #pragma unroll
-    for (int t = 0; t < BQ / 16; ++t)
+      for (int t = 0; t < BQ / 16; ++t)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int col = (t >> 1) * 32 + 8 * (2 * (t & 1) + hh) + 4 * g;
-        const bf16x4 v4 = {dsb[t][4 * hh], dsb[t][4 * hh + 1], dsb[t][4 * hh + 2], dsb[t][4 * hh + 3]};
-        *(bf16x4*)(sS + tile_off<SRC>(key_l, col * 2)) = v4;
-      }
-    __syncthreads();
-
-    // ---- dQ_i += scale * dS K_j (fp32 atomics) --------------------------------
-#pragma unroll
-    for (int u = 0; u < NDQ; ++u) {
-      const int bi = w + T::NW * u;
-      const int qb = bi / NDB, db = bi % NDB;
-      if (!CAUSAL || q0 + qb * 32 + 31 >= kv0) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int t = 0; t < BKV / 16; ++t) {
-          const char* sb = sS + 16 * t * T::SROWB;
-          const char* kb = sK + 16 * t * QROWB;
-          const short4v slo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][0]));
-          const short4v shi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][1]));
-          const short4v klo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][0]));
-          const short4v khi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][1]));
-          acc = mfma_bf16(cat4(slo, shi), cat4(klo, khi), acc);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int col = (t >> 1) * 32 + 8 * (2 * (t & 1) + hh) + 4 * g;
+          const bf16x4 v4 = {dsb[t][4 * hh], dsb[t][4 * hh + 1], dsb[t][4 * hh + 2], dsb[t][4 * hh + 3]};
+          *(bf16x4*)(sS + tile_off<SRC>(key_l, col * 2)) = v4;
         }
-        float* dqh = a.dq + qhead * D;
+      __syncthreads();
+
+      // ---- dQ_i += scale * dS K_j (fp32 atomics) --------------------------------
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (qrow < a.Nq) atomicAdd(dqh + (size_t)qrow * D + db * 32 + l32, scale * acc[r]);
+      for (int u = 0; u < NDQ; ++u) {
+        const int bi = w + T::NW * u;
+        const int qb = bi / NDB, db = bi % NDB;
+        if (!CAUSAL || q0 + qb * 32 + 31 >= kv0) {
+          f32x16 acc = f32x16{};
+#pragma unroll
+          for (int t = 0; t < BKV / 16; ++t) {
+            const char* sb = sS + 16 * t * T::SROWB;
+            const char* kb = sK + 16 * t * QROWB;
+            const short4v slo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][0]));
+            const short4v shi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(sb + tsoff[qb][1]));
+            const short4v klo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][0]));
+            const short4v khi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kb + troff[db][1]));
+            acc = mfma_bf16(cat4(slo, shi), cat4(klo, khi), acc);
+          }
+          float* dqh = a.dq + qhead * D;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (qrow < a.Nq) atomicAdd(dqh + (size_t)qrow * D + db * 32 + l32, scale * acc[r]);
+          }
         }
       }
     }
@@ -396,37 +406,248 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool GF32>
+// ---------------------------------------------------------------------------
+// second pass: dQ_i = scale * sum_j dS_ij K_j, Q-outer like the forward
+// ---------------------------------------------------------------------------
+//
+// The alternative to atomic dQ that page 6.2 section 7.2 names: each
+// workgroup owns one Q tile (4 wavefronts x 32 rows, B_r = 128) and walks the
+// K/V tiles up to the diagonal, recomputing S, P, dP and dS, so dQ is summed in
+// registers and written once (no atomics, no zeroing, deterministic). As in
+// the forward, the products are transposed so that each lane owns one query:
+// S^T = K Q^T and dP^T = V dO^T take Q and dO as register B operands, L and D
+// are per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from the
+// accumulator registers and K^T by transpose reads of the K tile.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4, BR = 32 * NW, BC = 64, NKB = BC / 32;
+  constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB, CPW = TILEB / (1024 * NW);
+  constexpr int NKK = D / 16, NDB = D / 32;
+  static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole wave loads");
+
+  __shared__ __attribute__((aligned(16))) char sK0[TILEB];
+  __shared__ __attribute__((aligned(16))) char sV0[TILEB];
+  __shared__ __attribute__((aligned(16))) char sK1[TILEB];
+  __shared__ __attribute__((aligned(16))) char sV1[TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int j16 = lane & 15;
+
+  const int n_q_tiles = ceil_div(a.Nq, BR);
+  const int heads = a.B * a.Hq;
+  const int slot = blockIdx.x % heads;
+  const int rank = blockIdx.x / heads;
+  const int bkv_n = a.B * a.Hkv;
+  const int bkv = slot % bkv_n;
+  const int member = slot / bkv_n;
+  const int b = bkv / a.Hkv;
+  const int hkv = bkv % a.Hkv;
+  const int hq = hkv * a.G + member;
+  const int qt = CAUSAL ? (n_q_tiles - 1 - rank) : rank;
+  const int q0 = qt * BR;
+  const int q0w = q0 + 32 * w;
+  const int qrow = q0w + l32;
+
+  const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
+  const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
+
+  bf16x8 qf[NKK], dof[NKK];
+  {
+    const char* Qr = (const char*)a.q + (qhead + qrow) * ROWB;
+    const char* Or = (const char*)a.dout + (qhead + qrow) * ROWB;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (qrow < a.Nq) {
+        x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
+        y = *(const u32x4*)(Or + (kk * 16 + 8 * g) * 2);
+      }
+      qf[kk] = __builtin_bit_cast(bf16x8, x);
+      dof[kk] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  // Rows past the end get L = +inf, so their P (and dS) is 0.
+  const float l2 = qrow < a.Nq ? a.lse[qhead + qrow] * kLog2e : INFINITY;
+  const float dq_d = qrow < a.Nq ? a.dvec[qhead + qrow] : 0.0f;
+
+  const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
+  const int n_kv = ceil_div(kv_end, BC);
+
+  auto issue_tile = [&](int jt, char* Kt, char* Vt) {
+    const int kv0 = jt * BC;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int cb = (w * CPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / RC, pc = idx % RC;
+      const int lc = pc ^ swz<RC>(row);
+      const size_t off = (size_t)min(kv0 + row, a.Nk - 1) * ROWB + lc * 16;
+      load_lds_16(Kh + off, Kt + cb * 16);
+      load_lds_16(Vh + off, Vt + cb * 16);
+    }
+  };
+
+  int koff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
+  int troff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      troff[db][h] = tile_off<RC>(4 * g + 8 * h + (j16 >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+  const float c = a.c;
+
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kv0 = jt * BC;
+    f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
+      dpacc[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        sacc[kb] = mfma_bf16(*(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB), qf[kk], sacc[kb]);
+        dpacc[kb] = mfma_bf16(*(const bf16x8*)(Vt + koff[kk] + kb * 32 * ROWB), dof[kk], dpacc[kb]);
+      }
+    }
+    // P^T = exp2(S^T c - L log2 e), dS^T = P^T o (dP^T - D)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
+        if constexpr (MASK) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
+          p = vis ? p : 0.0f;
+        }
+        sacc[kb][r] = p * (dpacc[kb][r] - dq_d);
+      }
+    // dQ^T += K^T dS^T: slot (g, v) of step t holds key 16t + 8*(v/4) + 4g + v%4
+#pragma unroll
+    for (int t = 0; t < BC / 16; ++t) {
+      float sv[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) sv[v] = sacc[t >> 1][8 * (t & 1) + v];
+      const bf16x8 sb = to_bf16x8(sv);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* kp = Kt + 16 * t * ROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][1]));
+        dqacc[db] = mfma_bf16(cat4(lo, hi), sb, dqacc[db]);
+      }
+    }
+  };
+
+  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) {
+    const int kv0 = jt * BC;
+    if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
+    const bool active = !CAUSAL || kv0 <= q0w + 31;
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
+    if (active) {
+      if (need_mask)
+        body(std::true_type{}, jt, Kt, Vt);
+      else
+        body(std::false_type{}, jt, Kt, Vt);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  issue_tile(0, sK0, sV0);
+  wait_vmem();
+  __syncthreads();
+  int jt = 0;
+  for (; jt + 1 < n_kv; jt += 2) {
+    step(jt, sK0, sV0, sK1, sV1);
+    step(jt + 1, sK1, sV1, sK0, sV0);
+  }
+  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
+
+  if (qrow < a.Nq) {
+    float* dqr = a.dq + (qhead + qrow) * D;
+    const float scale = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 v = {scale * dqacc[db][4 * a4], scale * dqacc[db][4 * a4 + 1], scale * dqacc[db][4 * a4 + 2],
+                         scale * dqacc[db][4 * a4 + 3]};
+        *(f32x4*)(dqr + db * 32 + 8 * a4 + 4 * g) = v;
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool GF32, bool ATOMIC_DQ>
 static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
   using T = BwdTile<D>;
-  auto kern = bwd_kernel<D, CAUSAL, GF32>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  constexpr int lds = ATOMIC_DQ ? T::LDS_BYTES_ATOMIC : T::LDS_BYTES_SPLIT;
+  auto kern = bwd_kernel<D, CAUSAL, GF32, ATOMIC_DQ>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::NT), T::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(T::NT), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_all(const BwdArgs& a, bool o_f32, bool atomic_dq, hipStream_t s) {
   const long long rows = (long long)a.B * a.Hq * a.Nq;
   const long long threads = rows * (D / 8);
   const unsigned pblocks = (unsigned)((threads + 255) / 256);
-  if (o_f32)
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D, true>), dim3(pblocks), dim3(256), 0, s, (const __bf16*)a.dout, a.o,
-                       a.dvec, a.dq, rows);
-  else
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D, false>), dim3(pblocks), dim3(256), 0, s, (const __bf16*)a.dout, a.o,
-                       a.dvec, a.dq, rows);
+  const __bf16* dout = (const __bf16*)a.dout;
+  if (o_f32) {
+    if (atomic_dq)
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, true>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+    else
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+  } else {
+    if (atomic_dq)
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, true>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+    else
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (causal) return grad_f32 ? launch_bwd_main<D, true, true>(a, s) : launch_bwd_main<D, true, false>(a, s);
-  return grad_f32 ? launch_bwd_main<D, false, true>(a, s) : launch_bwd_main<D, false, false>(a, s);
+  if (atomic_dq) return launch_bwd_main<D, CAUSAL, GF32, true>(a, s);
+  e = launch_bwd_main<D, CAUSAL, GF32, false>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq<D, CAUSAL>(a, s);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
-  return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, s)
-                        : launch_bwd_d<128>(a, causal, o_f32, grad_f32, s);
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, bool atomic_dq, hipStream_t s) {
+  if (causal)
+    return grad_f32 ? launch_bwd_all<D, true, true>(a, o_f32, atomic_dq, s)
+                    : launch_bwd_all<D, true, false>(a, o_f32, atomic_dq, s);
+  return grad_f32 ? launch_bwd_all<D, false, true>(a, o_f32, atomic_dq, s)
+                  : launch_bwd_all<D, false, false>(a, o_f32, atomic_dq, s);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
+                      hipStream_t s) {
+  return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, atomic_dq, s)
+                        : launch_bwd_d<128>(a, causal, o_f32, grad_f32, atomic_dq, s);
 }
 
 }  // namespace fa

@@ -35,6 +35,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool in_f32, bool causal, bool out_f32, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
+                      hipStream_t s);
 
 }  // namespace fa

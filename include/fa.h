@@ -95,13 +95,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   dQ = scale * dS K; dK = scale * dS^T Q;
  * with dK, dV summed over the query heads of each K/V head group.
  *
+ * Scheme: D is computed once by a preprocess kernel (section 7.3); dK and dV
+ * by workgroups that each own one K/V column block (section 7.2); dQ by a
+ * second pass over Q tiles (the "two-pass" alternative to atomics that
+ * section 7.2 names), so no atomics are used and every output is
+ * deterministic. fa_bwd_atomic below is the single-pass variant.
+ *
  *   q, dout  [B][Hq][Nq][d] in_dtype (must be FA_DTYPE_BF16), read only
  *   k, v     [B][Hkv][Nk][d] in_dtype, read only
  *   o        [B][Hq][Nq][d] o_dtype (bf16 or fp32), the forward output
  *   lse      [B][Hq][Nq] fp32, the forward logsumexp
- *   dq       [B][Hq][Nq][d] fp32, fully overwritten (zeroed, then accumulated
- *            atomically across K/V column blocks; the last bits depend on the
- *            order of the atomic adds)
+ *   dq       [B][Hq][Nq][d] fp32, fully overwritten
  *   dk, dv   [B][Hkv][Nk][d] grad_dtype (bf16 or fp32), fully overwritten
  *   workspace  device buffer of at least fa_bwd_workspace_bytes() bytes; on
  *            return it holds D as fp32 [B][Hq][Nq]
@@ -114,7 +118,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
            int in_dtype, int o_dtype, int grad_dtype, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: 4 * batch * n_q_heads * seqlen_q
+/*
+ * fa_bwd_atomic — the same computation, arguments and results as fa_bwd, in
+ * a single pass: the K/V-column-block workgroups also form dQ_i = dS K_j for
+ * every Q block they visit and add it to dq with fp32 atomics (page 6.2,
+ * section 7.2; CSDN article, "并行性 / 反向传播"); the preprocess kernel
+ * zeroes dq first. Fewer matrix products than fa_bwd, but the atomic traffic
+ * is (number of K/V blocks) * seqlen_q * head_dim * 4 bytes per query head,
+ * and the last bits of dq depend on the order of the atomic adds.
+ */
+int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, float* dq, void* dk,
+                  void* dv, float* workspace, int batch, int n_q_heads,
+                  int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim,
+                  float scale, int causal, int in_dtype, int o_dtype,
+                  int grad_dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd and fa_bwd_atomic need: 4 * batch * n_q_heads * seqlen_q
  * (the fp32 vector D, page 6.2 section 7.3). Returns 0 for non-positive
  * arguments. */
 size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q);

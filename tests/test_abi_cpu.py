@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_last_error", "fa_status_string", "fa_version"])
+        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_workspace_bytes", "fa_fwd", "fa_last_error", "fa_status_string",
+         "fa_version"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -124,6 +125,12 @@ def test_fwd_argument_errors(lib, kw, code, text):
 ])
 def test_bwd_argument_errors(lib, kw, code, text):
     assert bwd(**kw) == code
+    assert text in binding.fa_last_error()
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, batch=1, n_q_heads=2, n_kv_heads=1,
+                seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
+                stream=None)
+    args.update(kw)
+    assert binding.fa_bwd_atomic(*args.values()) == code
     assert text in binding.fa_last_error()
 
 

@@ -53,12 +53,13 @@ def rounding_bounds(inp, scale, causal):
     return U_BF16 * bq, U_BF16 * bk, U_BF16 * bv
 
 
-def run_fwd_bwd(inp, scale, causal, grad_f32=True):
+def run_fwd_bwd(inp, scale, causal, grad_f32=True, atomic_dq=False):
     import torch
     q, k, v, do = upload(inp)
     o, lse = binding.forward(q, k, v, scale, causal, out_dtype=torch.float32)
     dq, dk, dv, dvec = binding.backward(q, k, v, o, lse, do, scale, causal,
-                                        grad_dtype=torch.float32 if grad_f32 else torch.bfloat16)
+                                        grad_dtype=torch.float32 if grad_f32 else torch.bfloat16,
+                                        atomic_dq=atomic_dq)
     torch.cuda.synchronize()
     return host(o), host(lse), host(dq), host(dk), host(dv), host(dvec)
 
@@ -78,13 +79,14 @@ CASES = [
 IDS = [f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}" for c in CASES]
 
 
+@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic"])
 @pytest.mark.parametrize("case", CASES, ids=IDS)
-def test_bwd_parity(case):
+def test_bwd_parity(case, atomic_dq):
     B, Hq, Hkv, Nq, Nk, d, causal = case
-    announce(f"bwd {case}")
+    announce(f"bwd {case} atomic_dq={atomic_dq}")
     inp = gen(300 + Nq + d, B, Hq, Hkv, Nq, Nk, d, with_do=True)
     scale = float(np.float32(1 / math.sqrt(d)))
-    O, L, dQ, dK, dV, Dv = run_fwd_bwd(inp, scale, causal)
+    O, L, dQ, dK, dV, Dv = run_fwd_bwd(inp, scale, causal, atomic_dq=atomic_dq)
     dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
     bq, bk, bv = rounding_bounds(inp, scale, causal)
     assert np.all(np.abs(dQ - dQr) <= TOL + bq), "dQ"
@@ -99,11 +101,12 @@ def test_bwd_parity(case):
     assert np.max(np.abs(dV.sum(axis=2) - ref)) <= 0.05 + 1e-3 * np.max(np.abs(ref))
 
 
-def test_bwd_bf16_grads():
-    announce("bwd bf16 grads")
+@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic"])
+def test_bwd_bf16_grads(atomic_dq):
+    announce(f"bwd bf16 grads atomic_dq={atomic_dq}")
     inp = gen(41, 1, 4, 2, 300, 300, 128, with_do=True)
     scale = float(np.float32(1 / math.sqrt(128)))
-    _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, scale, True, grad_f32=False)
+    _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, scale, True, grad_f32=False, atomic_dq=atomic_dq)
     dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, True)
     bq, bk, bv = rounding_bounds(inp, scale, True)
     assert np.all(np.abs(dQ - dQr) <= TOL + bq)
@@ -111,11 +114,27 @@ def test_bwd_bf16_grads():
     assert np.all(np.abs(dV - dVr) <= TOL + bv + bf16_half_ulp(dVr))
 
 
-def test_bwd_zero_scale():
-    announce("bwd scale 0")
+@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic"])
+def test_bwd_zero_scale(atomic_dq):
+    announce(f"bwd scale 0 atomic_dq={atomic_dq}")
     inp = gen(42, 1, 2, 1, 150, 150, 64, with_do=True)
     for causal in (False, True):
-        _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, 0.0, causal)
+        _, _, dQ, dK, dV, _ = run_fwd_bwd(inp, 0.0, causal, atomic_dq=atomic_dq)
         assert np.all(dQ == 0.0) and np.all(dK == 0.0)
         _, _, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, 0.0, causal)
         assert np.max(np.abs(dV - dVr)) <= TOL
+
+
+def test_bwd_two_pass_is_deterministic():
+    """fa_bwd uses no atomics: two runs give bitwise identical gradients."""
+    import torch
+    announce("bwd determinism")
+    inp = gen(43, 2, 4, 2, 700, 700, 128, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    q, k, v, do = upload(inp)
+    o, lse = binding.forward(q, k, v, scale, True, out_dtype=torch.float32)
+    r1 = binding.backward(q, k, v, o, lse, do, scale, True, grad_dtype=torch.float32)
+    r2 = binding.backward(q, k, v, o, lse, do, scale, True, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
