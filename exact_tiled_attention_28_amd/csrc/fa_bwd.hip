@@ -132,13 +132,13 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int j16 = lane & 15;
 
-  // Work decode: (batch, kv head) fastest, K/V blocks from the first (the
-  // heaviest under the causal mask) to the last.
-  const int bkv_n = a.B * a.Hkv;
-  const int bkv = blockIdx.x % bkv_n;
-  const int jblk = blockIdx.x / bkv_n;
-  const int b = bkv / a.Hkv;
-  const int hkv = bkv % a.Hkv;
+  // Work decode: a unit is one (batch, K/V head), its items the K/V blocks
+  // from the first (the heaviest under the causal mask) to the last;
+  // units vary fastest (xcd_decode).
+  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
+  const int b = ui.unit / a.Hkv;
+  const int hkv = ui.unit % a.Hkv;
+  const int jblk = ui.item;
   const int kv0 = jblk * BKV;
   const int key_l = 32 * w + l32;  // this lane's key inside the block
   const int key = kv0 + key_l;
@@ -171,9 +171,8 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     }
   }
 
-  // Per-lane LDS byte offsets, computed once. Row swizzles repeat every 16
-  // rows (32 for 8-chunk rows), so whole 32-row blocks and 16-row steps only
-  // add constants.
+  // Per-lane LDS byte offsets, computed once. Row swizzles repeat every 8
+  // rows, so whole 32-row blocks and 16-row steps only add constants.
   int qoff[NKK];  // A operand rows of Q / dO: row l32, head-dim step kk
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qoff[kk] = tile_off<QRC>(l32, (kk * 16 + 8 * g) * 2);
@@ -207,7 +206,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   // ---- Q_i / dO_i tiles: HBM -> swizzled LDS without registers; L_i, D_i
   // through registers (rows past the end get L = +inf, so P = 0 there) ----
   float lr = 0.0f, dr = 0.0f;
-  auto issue_q = [&](int it, int buf) {
+  auto issue_q = [&](int it, int buf) __attribute__((always_inline)) {
     const int hm = it / n_i;
     const int i = i_first + it % n_i;
     const int hq = hkv * a.G + hm;
@@ -231,7 +230,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
       dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
     }
   };
-  auto store_ld = [&](int buf) {
+  auto store_ld = [&](int buf) __attribute__((always_inline)) {
     if (tid < BQ) {
       sL[buf * BQ + tid] = lr;
       sD[buf * BQ + tid] = dr;
@@ -438,15 +437,11 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   const int j16 = lane & 15;
 
   const int n_q_tiles = ceil_div(a.Nq, BR);
-  const int heads = a.B * a.Hq;
-  const int slot = blockIdx.x % heads;
-  const int rank = blockIdx.x / heads;
-  const int bkv_n = a.B * a.Hkv;
-  const int bkv = slot % bkv_n;
-  const int member = slot / bkv_n;
-  const int b = bkv / a.Hkv;
-  const int hkv = bkv % a.Hkv;
-  const int hq = hkv * a.G + member;
+  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
+  const int b = ui.unit / a.Hkv;
+  const int hkv = ui.unit % a.Hkv;
+  const int rank = ui.item / a.G;
+  const int hq = hkv * a.G + ui.item % a.G;
   const int qt = CAUSAL ? (n_q_tiles - 1 - rank) : rank;
   const int q0 = qt * BR;
   const int q0w = q0 + 32 * w;
@@ -479,7 +474,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
-  auto issue_tile = [&](int jt, char* Kt, char* Vt) {
+  auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
@@ -508,7 +503,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
 
-  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) {
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
     f32x16 sacc[NKB], dpacc[NKB];
@@ -552,7 +547,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) {
+  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
     if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
     const bool active = !CAUSAL || kv0 <= q0w + 31;
@@ -636,7 +631,8 @@ static hipError_t launch_bwd_all(const BwdArgs& a, bool o_f32, bool atomic_dq, h
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, bool atomic_dq, hipStream_t s) {
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
+                               hipStream_t s) {
   if (causal)
     return grad_f32 ? launch_bwd_all<D, true, true>(a, o_f32, atomic_dq, s)
                     : launch_bwd_all<D, true, false>(a, o_f32, atomic_dq, s);

@@ -65,16 +65,22 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
   return __builtin_convertvector(v, bf16x8);
 }
 
-// LDS tiles hold rows of `row_chunks` 16-byte chunks. Chunk c of row r is
-// stored at chunk position c ^ swz(r) so that the 16 rows read together by
-// one MFMA operand fetch fall in distinct banks.
+// LDS tiles hold rows of ROW_CHUNKS 16-byte chunks (ROW_CHUNKS >= 8, rows a
+// multiple of 128 bytes, so every row starts on the same bank). Chunk c of
+// row r is stored at chunk position c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2,
+// so that the LDS reads of the kernels touch distinct banks (128 bytes per
+// cycle):
+//  - ds_read_b128 of 8 consecutive rows at one logical chunk: swz takes 8
+//    distinct values over any 8 consecutive rows aligned to 8;
+//  - ds_read_b64_tr_b16 of a 16-lane block: 4 consecutive rows (aligned to
+//    4) x 2 adjacent chunks (an even chunk and the next): the XOR with
+//    2*(r%4) moves the pair to 4 distinct even/odd chunk pairs.
+// swz depends only on r % 8, so moving by whole 8-row steps keeps every
+// lane's chunk position.
 template <int ROW_CHUNKS>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (ROW_CHUNKS >= 16) {
-    return row & 15;
-  } else {
-    return (row >> (4 - __builtin_ctz(ROW_CHUNKS))) & (ROW_CHUNKS - 1);
-  }
+  static_assert(ROW_CHUNKS >= 8, "rows of at least 128 bytes");
+  return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 // Byte offset of (row, byte-in-row) inside a swizzled LDS tile.

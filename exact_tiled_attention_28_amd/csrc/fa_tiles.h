@@ -38,4 +38,16 @@ constexpr int kv_tiles_for(int q0, int nq, int seqlen_k, int bc, bool causal) {
 // at the diagonal).
 constexpr int first_q_tile_for(int k0, int br, bool causal) { return causal ? k0 / br : 0; }
 
+// Workgroup -> work-item decode. The work is organised in units (one
+// (batch, K/V head) each) of `items` work items, items ordered heaviest
+// first. Units vary fastest: all units' first (heaviest) items are dispatched
+// first, then all second items, and so on. Workgroups are dispatched
+// round-robin over the 8 XCDs of an MI355X (WG L runs on XCD L % 8), so when
+// the number of units is a multiple of 8 every workgroup of a unit runs on
+// XCD unit % 8 and the unit's K/V stays in that XCD's L2.
+struct UnitItem {
+  int unit, item;
+};
+constexpr UnitItem xcd_decode(int L, int units) { return UnitItem{L % units, L / units}; }
+
 }  // namespace fa

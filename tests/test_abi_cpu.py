@@ -167,6 +167,12 @@ int main() {
         for (int q0 = 0; q0 < n; q0 += br)
           std::printf("K %d %d %d %d %d %d %d\n", n, br, bc, q0, fa::kv_tiles_for(q0, br, n, bc, true),
                       fa::kv_tiles_for(q0, br, n, bc, false), fa::first_q_tile_for(q0, br, true));
+  for (int units = 1; units <= 48; units += 1)
+    for (int items = 1; items <= 9; items += 4)
+      for (int L = 0; L < units * items; ++L) {
+        fa::UnitItem u = fa::xcd_decode(L, units);
+        std::printf("X %d %d %d %d %d\n", units, items, L, u.unit, u.item);
+      }
   return 0;
 }
 """
@@ -182,8 +188,16 @@ def test_tile_bookkeeping_matches_brute_force():
         assert r.returncode == 0, r.stderr
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.splitlines()
     n_cls = n_trip = 0
+    seen = {}
     for ln in lines:
         f = ln.split()
+        if f[0] == "X":
+            units, items, L, unit, item = map(int, f[1:])
+            assert 0 <= unit < units and 0 <= item < items
+            seen.setdefault((units, items), set()).add((unit, item))
+            if units % 8 == 0:
+                assert unit % 8 == L % 8, "a unit must stay on one XCD (L % 8)"
+            continue
         if f[0] == "K":
             n, br, bc, q0, trips_c, trips_n, first = map(int, f[1:])
             rows = range(q0, min(n, q0 + br))
@@ -201,3 +215,5 @@ def test_tile_bookkeeping_matches_brute_force():
         assert cls == expect, (q0, nq, k0, nk)
         n_cls += 1
     assert n_cls > 500 and n_trip > 500
+    for (units, items), pairs in seen.items():
+        assert len(pairs) == units * items, "xcd_decode must be a bijection"

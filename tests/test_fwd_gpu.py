@@ -101,3 +101,26 @@ def test_fwd_scale_edge_cases(scale):
         Or, Lr = oracle.forward(inp.q, inp.k, inp.v, scale, causal)
         assert np.max(np.abs(O - Or)) <= O_TOL_BF16
         assert np.max(np.abs(L - Lr)) <= L_TOL_BF16
+
+
+# Shapes with >= 4096 keys take the two-group (ping-pong) bf16 kernel; ragged
+# lengths, both head dims, GQA and Nq != Nk exercise its tiling and masks.
+LONG_CASES = [
+    (1, 2, 1, 4097, 4097, 128, True),
+    (1, 2, 2, 4100, 4100, 64, True),
+    (1, 2, 1, 333, 4200, 128, False),
+    (1, 1, 1, 4096, 4096, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES,
+                         ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}" for c in LONG_CASES])
+def test_fwd_long_keys_parity(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    announce(f"fwd bf16 long {case}")
+    inp = gen(400 + Nq + d, B, Hq, Hkv, Nq, Nk, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L = run_fwd(inp, scale, causal)
+    Or, Lr = oracle.forward(inp.q, inp.k, inp.v, scale, causal)
+    assert np.max(np.abs(O - Or)) <= O_TOL_BF16
+    assert np.max(np.abs(L - Lr)) <= L_TOL_BF16
