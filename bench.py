@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the run, copy a MIB-MiB buffer 3 times (a plain copy kernel of known size, to "
+                        "scale the HBM byte counters of a profiler run)")
     return p.parse_args()
 
 
@@ -134,6 +137,27 @@ def time_calls(step, calls, steps, warmup):
     return per_step, per_call, wall
 
 
+def measured_traffic(call):
+    """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
+    have changed since they were taken."""
+    import hashlib
+    csrc = os.path.join(ROOT, "exact_tiled_attention_28_amd", "csrc")
+    rec_path = os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(rec_path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sources_sha256") != h.hexdigest() or call not in rec:
+        return None
+    return rec[call]["fetch_bytes"] + rec[call]["write_bytes"]
+
+
 def cpu_baseline(w, inp, heads):
     """The fp64 oracle, untuned, on `heads` (batch, head) slices of the
     workload: forward + backward. Returns the JSON object."""
@@ -192,9 +216,9 @@ def main():
     avg_bwd = float(np.mean(per_call[:, 1]))
     if avg_bwd >= avg_fwd:
         dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_kernel + bwd_dq_kernel, one call)", "flops": bf,
-               "ms": avg_bwd}
+               "ms": avg_bwd, "traffic": measured_traffic("fa_bwd")}
     else:
-        dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd}
+        dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd, "traffic": measured_traffic("fa_fwd")}
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -227,12 +251,27 @@ def main():
         "wall_ms_per_step": round(wall, 4),
         "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": dom["traffic"],
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "avg_launch_ms": round(dom["ms"], 4)},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(out), flush=True)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+
+
+def copy_calibration(mib):
+    """dst.copy_(src) of `mib` MiB, three times: reads and writes exactly that
+    many bytes per launch."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": mib << 20}), flush=True)
 
 
 def bench_one(args):
