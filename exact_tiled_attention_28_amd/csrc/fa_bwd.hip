@@ -406,6 +406,301 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV pass of the two-pass scheme: 8 wavefronts, 2 per SIMD
+// ---------------------------------------------------------------------------
+//
+// Same method as bwd_kernel without dQ. The workgroup owns a K/V column block
+// of 128 keys; wavefront w takes keys 32*(w%4).. and query rows
+// 32*(w/4).. of every 64-row Q block, so each wavefront does 32 x 32 per
+// step and only 32 keys' dK, dV accumulate in its registers. K_j and V_j are
+// read from LDS as B operands (not held in registers), which keeps a
+// wavefront under 256 registers (2 per SIMD) with dK, dV in accumulation
+// registers. The two wavefronts that share keys sum their dK, dV through LDS
+// once at the end.
+template <int D>
+struct DkdvTile {
+  static constexpr int NW = 8;
+  static constexpr int BKV = 128, BQ = 64;
+  static constexpr int ROWB = D * 2, RC = ROWB / 16;
+  static constexpr int QTILEB = BQ * ROWB, KTILEB = BKV * ROWB;
+  static constexpr int QCPW = QTILEB / (1024 * NW);
+  static constexpr int KCPT = BKV * RC / (64 * NW);
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = OFF_K + KTILEB;
+  static constexpr int OFF_Q = OFF_V + KTILEB;        // [2][QTILEB]
+  static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;   // [2][QTILEB]
+  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;   // [2][BQ]
+  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;    // [2][BQ]
+  static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
+  static constexpr int RED_BYTES = 4 * (D / 32) * 16 * 64 * 4;  // one accumulator of the 4 key groups
+  static_assert(QTILEB % (1024 * NW) == 0 && (BKV * RC) % (64 * NW) == 0, "tiles must split evenly");
+  static_assert(RED_BYTES <= 4 * QTILEB, "the reduction buffer reuses the Q / dO tiles");
+};
+
+template <int D, bool CAUSAL, bool GF32>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdArgs a) {
+  using T = DkdvTile<D>;
+  constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB;
+  constexpr int QCPW = T::QCPW, KCPT = T::KCPT;
+  constexpr int NKK = D / 16, NDB = D / 32;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const sK = smem + T::OFF_K;
+  char* const sV = smem + T::OFF_V;
+  char* const sQ = smem + T::OFF_Q;
+  char* const sDO = smem + T::OFF_DO;
+  float* const sL = (float*)(smem + T::OFF_L);
+  float* const sD = (float*)(smem + T::OFF_D);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int kg = w & 3;   // key group: keys 32*kg.. of the block
+  const int qh = w >> 2;  // query half: rows 32*qh.. of each Q block
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int j16 = lane & 15;
+
+  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
+  const int b = ui.unit / a.Hkv;
+  const int hkv = ui.unit % a.Hkv;
+  const int kv0 = ui.item * BKV;
+  const int key = kv0 + 32 * kg + l32;  // this lane's key
+
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
+  const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
+
+  // K_j and V_j tiles (rows past the end are zero).
+#pragma unroll
+  for (int u = 0; u < KCPT; ++u) {
+    const int ci = tid + 64 * T::NW * u;
+    const int row = ci / RC, cc = ci % RC;
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (kv0 + row < a.Nk) {
+      const size_t off = (size_t)(kv0 + row) * ROWB + cc * 16;
+      x = *(const u32x4*)(Kh + off);
+      y = *(const u32x4*)(Vh + off);
+    }
+    const int lo = tile_off<RC>(row, cc * 16);
+    *(u32x4*)(sK + lo) = x;
+    *(u32x4*)(sV + lo) = y;
+  }
+
+  // Per-lane LDS offsets (row swizzles repeat every 8 rows).
+  int roff[NKK];  // row reads: row l32 of a 32-row block, head-dim step kk
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
+  int troff[NDB][2];  // transpose reads: column block db, half h
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      troff[db][h] = tile_off<RC>(4 * g + 8 * h + (j16 >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+
+  const int n_qblk = ceil_div(a.Nq, BQ);
+  const int i_first = first_q_tile_for(kv0, BQ, CAUSAL);
+  const int n_i = n_qblk - i_first;
+  const int total = a.G * n_i;
+  const float c = a.c;
+  const float scale = a.scale;
+
+  float lr = 0.0f, dr = 0.0f;
+  auto issue_q = [&](int it, int buf) __attribute__((always_inline)) {
+    const int hm = it / n_i;
+    const int i = i_first + it % n_i;
+    const int hq = hkv * a.G + hm;
+    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    const int q0 = i * BQ;
+    const char* Qh = (const char*)a.q + qhead * ROWB;
+    const char* Oh = (const char*)a.dout + qhead * ROWB;
+#pragma unroll
+    for (int u = 0; u < QCPW; ++u) {
+      const int cb = (w * QCPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / RC, pc = idx % RC;
+      const int lc = pc ^ swz<RC>(row);
+      const size_t off = (size_t)min(q0 + row, a.Nq - 1) * ROWB + lc * 16;
+      load_lds_16(Qh + off, sQ + buf * QTILEB + cb * 16);
+      load_lds_16(Oh + off, sDO + buf * QTILEB + cb * 16);
+    }
+    if (tid < BQ) {
+      const bool ok = q0 + tid < a.Nq;
+      lr = ok ? a.lse[qhead + q0 + tid] * kLog2e : INFINITY;
+      dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
+    }
+  };
+  auto store_ld = [&](int buf) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      sL[buf * BQ + tid] = lr;
+      sD[buf * BQ + tid] = dr;
+    }
+  };
+
+  if (total > 0) {
+    issue_q(0, 0);
+    store_ld(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  const char* const kTile = sK + kg * 32 * ROWB;
+  const char* const vTile = sV + kg * 32 * ROWB;
+
+  auto body = [&](auto mask_tag, int q0, const char* tQ, const char* tDO, const float* tL, const float* tD)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* qRows = tQ + qh * 32 * ROWB;
+    const char* oRows = tDO + qh * 32 * ROWB;
+    // S = Q K^T (query rows in registers, one key per lane)
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s = mfma_bf16(*(const bf16x8*)(qRows + roff[kk]), *(const bf16x8*)(kTile + roff[kk]), s);
+    // P = exp2(S c - L log2 e)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int r0 = qh * 32 + 8 * a4 + 4 * g;
+      const f32x4 lv = *(const f32x4*)(tL + r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(fmaf(s[4 * a4 + e], c, -lv[e]));
+        if constexpr (MASK) {
+          const bool vis = key < a.Nk && (!CAUSAL || key <= q0 + r0 + e);
+          p = vis ? p : 0.0f;
+        }
+        s[4 * a4 + e] = p;
+      }
+    }
+    bf16x8 pb[2];
+    {
+      float pv[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) pv[v] = s[8 * t + v];
+        pb[t] = to_bf16x8(pv);
+      }
+    }
+    // dV^T += dO^T P over this wave's 32 query rows (two 16-row steps)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* base = oRows + 16 * t * ROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+        dvacc[db] = mfma_bf16(cat4(lo, hi), pb[t], dvacc[db]);
+      }
+    // dP = dO V^T, dS = P o (dP - D)
+    f32x16 dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      dp = mfma_bf16(*(const bf16x8*)(oRows + roff[kk]), *(const bf16x8*)(vTile + roff[kk]), dp);
+    bf16x8 dsb[2];
+    {
+      float dsv[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 dv = *(const f32x4*)(tD + qh * 32 + 8 * a4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[4 * a4 + e] = s[4 * a4 + e] * (dp[4 * a4 + e] - dv[e]);
+      }
+      dsb[0] = to_bf16x8(dsv);
+      dsb[1] = to_bf16x8(dsv + 8);
+    }
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* base = qRows + 16 * t * ROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+        dkacc[db] = mfma_bf16(cat4(lo, hi), dsb[t], dkacc[db]);
+      }
+  };
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    const int i = i_first + it % n_i;
+    const int q0 = i * BQ;
+    const bool has_next = it + 1 < total;
+    if (has_next) issue_q(it + 1, buf ^ 1);
+    const char* tQ = sQ + buf * QTILEB;
+    const char* tDO = sDO + buf * QTILEB;
+    const float* tL = sL + buf * BQ;
+    const float* tD = sD + buf * BQ;
+    // Skip when all of this wavefront's keys lie after all of its queries.
+    const bool active = !CAUSAL || kv0 + 32 * kg <= q0 + 32 * qh + 31;
+    if (active) {
+      const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * qh) || (kv0 + 32 * kg + 32 > a.Nk);
+      if (need_mask)
+        body(std::true_type{}, q0, tQ, tDO, tL, tD);
+      else
+        body(std::false_type{}, q0, tQ, tDO, tL, tD);
+    }
+    if (has_next) store_ld(buf ^ 1);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- sum the two query halves' dK, dV through LDS, then store ------------
+  f32x4* red = (f32x4*)sQ;  // [kg][db][r/4][lane], reuses the Q / dO tiles
+  auto exchange = [&](f32x16 (&acc)[NDB]) __attribute__((always_inline)) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          red[((kg * NDB + db) * 4 + a4) * 64 + lane] =
+              f32x4{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 x = red[((kg * NDB + db) * 4 + a4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * a4 + e] += x[e];
+        }
+    }
+    __syncthreads();
+  };
+  exchange(dkacc);
+  exchange(dvacc);
+
+  if (qh == 0 && key < a.Nk) {
+    const size_t rowoff = (kvhead + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = db * 32 + 8 * a4 + 4 * g;
+        const f32x4 kv = {scale * dkacc[db][4 * a4], scale * dkacc[db][4 * a4 + 1], scale * dkacc[db][4 * a4 + 2],
+                          scale * dkacc[db][4 * a4 + 3]};
+        const f32x4 vv = {dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]};
+        if constexpr (GF32) {
+          *(f32x4*)((float*)a.dk + rowoff + d0) = kv;
+          *(f32x4*)((float*)a.dv + rowoff + d0) = vv;
+        } else {
+          *(bf16x4*)((__bf16*)a.dk + rowoff + d0) = __builtin_convertvector(kv, bf16x4);
+          *(bf16x4*)((__bf16*)a.dv + rowoff + d0) = __builtin_convertvector(vv, bf16x4);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // second pass: dQ_i = scale * sum_j dS_ij K_j, Q-outer like the forward
 // ---------------------------------------------------------------------------
 //
@@ -598,6 +893,17 @@ static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  using T = DkdvTile<D>;
+  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), T::LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
@@ -625,7 +931,7 @@ static hipError_t launch_bwd_all(const BwdArgs& a, bool o_f32, bool atomic_dq, h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (atomic_dq) return launch_bwd_main<D, CAUSAL, GF32, true>(a, s);
-  e = launch_bwd_main<D, CAUSAL, GF32, false>(a, s);
+  e = launch_bwd_dkdv<D, CAUSAL, GF32>(a, s);
   if (e != hipSuccess) return e;
   return launch_bwd_dq<D, CAUSAL>(a, s);
 }
