@@ -713,7 +713,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 // are per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from the
 // accumulator registers and K^T by transpose reads of the K tile.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 4, BR = 32 * NW, BC = 64, NKB = BC / 32;
   constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB, CPW = TILEB / (1024 * NW);
   constexpr int NKK = D / 16, NDB = D / 32;
@@ -769,17 +769,42 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
+  // This lane's 16-byte chunk of wave load u of a K/V tile, as a byte offset
+  // from the tile's first row. Loads u and u + 2 are 2 * (64 / RC) rows apart,
+  // a whole number of 8-row swizzle periods, so two offsets cover every load
+  // of a full tile; only a ragged last tile recomputes them with the clamp.
+  constexpr int RPL = 64 / RC;
+  static_assert((2 * RPL) % 8 == 0, "two wave loads must span whole swizzle periods");
+  int ldoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = (w * CPW + h) * 64 + lane;
+    const int row = idx / RC;
+    ldoff[h] = row * ROWB + (((idx % RC) ^ swz<RC>(row)) << 4);
+  }
   auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
+    if (kv0 + BC <= a.Nk) {
+      const char* Kb = Kh + (size_t)kv0 * ROWB;
+      const char* Vb = Vh + (size_t)kv0 * ROWB;
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int cb = (w * CPW + u) * 64;
-      const int idx = cb + lane;
-      const int row = idx / RC, pc = idx % RC;
-      const int lc = pc ^ swz<RC>(row);
-      const size_t off = (size_t)min(kv0 + row, a.Nk - 1) * ROWB + lc * 16;
-      load_lds_16(Kh + off, Kt + cb * 16);
-      load_lds_16(Vh + off, Vt + cb * 16);
+      for (int u = 0; u < CPW; ++u) {
+        const int cb = (w * CPW + u) * 64;
+        const int off = ldoff[u & 1] + (u >> 1) * 2 * RPL * ROWB;
+        load_lds_16(Kb + off, Kt + cb * 16);
+        load_lds_16(Vb + off, Vt + cb * 16);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int cb = (w * CPW + u) * 64;
+        const int idx = cb + lane;
+        const int row = idx / RC, pc = idx % RC;
+        const int lc = pc ^ swz<RC>(row);
+        const size_t off = (size_t)min(kv0 + row, a.Nk - 1) * ROWB + lc * 16;
+        load_lds_16(Kh + off, Kt + cb * 16);
+        load_lds_16(Vh + off, Vt + cb * 16);
+      }
     }
   };
 
@@ -798,47 +823,48 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
 
+  // One K/V tile, 32 keys at a time (block kb): S^T and dP^T for the block,
+  // then dS^T, then its share of dQ^T += K^T dS^T, so only one block's S^T,
+  // dP^T and dS^T are live at once.
   auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
-    f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
-      dpacc[kb] = f32x16{};
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sacc[kb] = mfma_bf16(*(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB), qf[kk], sacc[kb]);
-        dpacc[kb] = mfma_bf16(*(const bf16x8*)(Vt + koff[kk] + kb * 32 * ROWB), dof[kk], dpacc[kb]);
+        sacc = mfma_bf16(*(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB), qf[kk], sacc);
+        dpacc = mfma_bf16(*(const bf16x8*)(Vt + koff[kk] + kb * 32 * ROWB), dof[kk], dpacc);
       }
-    }
-    // P^T = exp2(S^T c - L log2 e), dS^T = P^T o (dP^T - D)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      // P^T = exp2(S^T c - L log2 e), dS^T = P^T o (dP^T - D)
+      float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(sacc[kb][r], c, -l2));
+        float p = fast_exp2(fmaf(sacc[r], c, -l2));
         if constexpr (MASK) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
           p = vis ? p : 0.0f;
         }
-        sacc[kb][r] = p * (dpacc[kb][r] - dq_d);
+        dsv[r] = p * (dpacc[r] - dq_d);
       }
-    // dQ^T += K^T dS^T: slot (g, v) of step t holds key 16t + 8*(v/4) + 4g + v%4
+      // dQ^T += K^T dS^T: slot (g, v) of step t holds key 16t + 8*(v/4) + 4g + v%4
 #pragma unroll
-    for (int t = 0; t < BC / 16; ++t) {
-      float sv[8];
+      for (int th = 0; th < 2; ++th) {
+        const bf16x8 sb = to_bf16x8(dsv + 8 * th);
+        const int t = 2 * kb + th;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) sv[v] = sacc[t >> 1][8 * (t & 1) + v];
-      const bf16x8 sb = to_bf16x8(sv);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const char* kp = Kt + 16 * t * ROWB;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][0]));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][1]));
-        dqacc[db] = mfma_bf16(cat4(lo, hi), sb, dqacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const char* kp = Kt + 16 * t * ROWB;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][0]));
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][1]));
+          dqacc[db] = mfma_bf16(cat4(lo, hi), sb, dqacc[db]);
+        }
       }
+      // Keep the next block's operand reads from being hoisted into this one
+      // (they would double the live operand registers).
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
