@@ -770,14 +770,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n_kv = ceil_div(kv_end, BC);
 
   // This lane's 16-byte chunk of wave load u of a K/V tile, as a byte offset
-  // from the tile's first row. Loads u and u + 2 are 2 * (64 / RC) rows apart,
-  // a whole number of 8-row swizzle periods, so two offsets cover every load
-  // of a full tile; only a ragged last tile recomputes them with the clamp.
+  // from the tile's first row. A wave load covers 64 / RC rows; NP loads span
+  // the 16-row swizzle period, so NP offsets cover every load of a full tile
+  // (load u adds whole periods to offset u % NP); only a ragged last tile
+  // recomputes them with the clamp.
   constexpr int RPL = 64 / RC;
-  static_assert((2 * RPL) % 8 == 0, "two wave loads must span whole swizzle periods");
-  int ldoff[2];
+  constexpr int NP = (16 / RPL < CPW) ? 16 / RPL : CPW;
+  static_assert(CPW % NP == 0 && (CPW == NP || (NP * RPL) % 16 == 0), "wave loads must tile whole swizzle periods");
+  int ldoff[NP];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NP; ++h) {
     const int idx = (w * CPW + h) * 64 + lane;
     const int row = idx / RC;
     ldoff[h] = row * ROWB + (((idx % RC) ^ swz<RC>(row)) << 4);
@@ -790,7 +792,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
         const int cb = (w * CPW + u) * 64;
-        const int off = ldoff[u & 1] + (u >> 1) * 2 * RPL * ROWB;
+        const int off = ldoff[u % NP] + (u / NP) * NP * RPL * ROWB;
         load_lds_16(Kb + off, Kt + cb * 16);
         load_lds_16(Vb + off, Vt + cb * 16);
       }

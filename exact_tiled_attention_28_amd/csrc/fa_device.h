@@ -66,21 +66,29 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 }
 
 // LDS tiles hold rows of ROW_CHUNKS 16-byte chunks (ROW_CHUNKS >= 8, rows a
-// multiple of 128 bytes, so every row starts on the same bank). Chunk c of
-// row r is stored at chunk position c ^ swz(r), swz(r) = 2*(r%4) + (r/4)%2,
-// so that the LDS reads of the kernels touch distinct banks (128 bytes per
-// cycle):
-//  - ds_read_b128 of 8 consecutive rows at one logical chunk: swz takes 8
-//    distinct values over any 8 consecutive rows aligned to 8;
-//  - ds_read_b64_tr_b16 of a 16-lane block: 4 consecutive rows (aligned to
-//    4) x 2 adjacent chunks (an even chunk and the next): the XOR with
-//    2*(r%4) moves the pair to 4 distinct even/odd chunk pairs.
-// swz depends only on r % 8, so moving by whole 8-row steps keeps every
-// lane's chunk position.
+// multiple of 128 bytes). Chunk c of row r is stored at chunk position
+// c ^ swz(r). The gfx950 LDS serves 64 banks of 4 bytes (256 bytes) per
+// cycle; swz is chosen so that the two operand reads of the kernels touch
+// 64 distinct banks in every cycle:
+//  - ds_read_b128 (16 lanes per cycle): 16 consecutive rows, aligned to 16,
+//    at one logical chunk must land on 16 distinct 16-byte bank groups;
+//  - ds_read_b64_tr_b16 (32 lanes per cycle): 4 consecutive rows, aligned to
+//    4, times an aligned block of 4 chunks must land on 16 distinct groups,
+//    so the 4 rows must move the block to 4 different blocks.
+// 256-byte rows (16 chunks): swz(r) = 4*(r%4) + (r/4)%4 - a bijection on
+// r % 16 whose block index (swz / 4) differs across any 4 aligned rows.
+// 128-byte rows (8 chunks): two rows share a 256-byte bank period and the
+// row parity selects its half; swz(r) = 4*((r/2)%2) + (r/4)%4 is a bijection
+// on bits 1-3 of r, and rows r and r+2 of any 4 aligned rows (same parity)
+// get different blocks.
+// swz depends only on r % 16, so moving by whole 16-row steps keeps every
+// lane's chunk position; all kernels step their per-lane offsets by multiples
+// of 16 rows.
 template <int ROW_CHUNKS>
 __device__ __forceinline__ int swz(int row) {
   static_assert(ROW_CHUNKS >= 8, "rows of at least 128 bytes");
-  return ((row & 3) << 1) | ((row >> 2) & 1);
+  if constexpr (ROW_CHUNKS >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 // Byte offset of (row, byte-in-row) inside a swizzled LDS tile.
