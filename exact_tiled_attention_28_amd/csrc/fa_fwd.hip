@@ -72,6 +72,7 @@ fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known to be wave-uniform
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
@@ -121,18 +122,44 @@ fwd_kernel(FwdArgs a) {
   // Wave w fills chunks [64*(w*CPW+u), +64) of each tile; chunk p of row r
   // holds logical chunk p ^ swz(r). Rows past the end of K/V repeat the last
   // row (their scores are masked).
+  // This lane's 16-byte chunk of wave load u, as a byte offset from the
+  // tile's first row: a wave load covers 64 / RC rows and NP loads span the
+  // 16-row swizzle period, so NP offsets cover every load of a full tile;
+  // only a ragged last tile recomputes them with the clamp.
+  constexpr int RPL = 64 / RC;
+  constexpr int NP = (16 / RPL < CPW) ? 16 / RPL : CPW;
+  static_assert(CPW % NP == 0 && (CPW == NP || (NP * RPL) % 16 == 0), "wave loads must tile whole swizzle periods");
+  int ldoff[NP];
+#pragma unroll
+  for (int h = 0; h < NP; ++h) {
+    const int idx = (wu * CPW + h) * 64 + lane;
+    const int row = idx / RC;
+    ldoff[h] = row * ROWB + (((idx % RC) ^ swz<RC>(row)) << 4);
+  }
   auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
+    if (kv0 + BC <= a.Nk) {
+      const char* Kb = Kh + (size_t)kv0 * ROWB;
+      const char* Vb = Vh + (size_t)kv0 * ROWB;
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int cb = (w * CPW + u) * 64;
-      const int idx = cb + lane;
-      const int row = idx / RC, pc = idx % RC;
-      const int lc = pc ^ swz<RC>(row);
-      const int grow = min(kv0 + row, a.Nk - 1);
-      const size_t off = (size_t)grow * ROWB + lc * 16;
-      load_lds_16(Kh + off, Kt + cb * 16);
-      load_lds_16(Vh + off, Vt + cb * 16);
+      for (int u = 0; u < CPW; ++u) {
+        const int cb = (wu * CPW + u) * 64;
+        const unsigned off = (unsigned)(ldoff[u % NP] + (u / NP) * NP * RPL * ROWB);
+        load_lds_16(Kb + off, Kt + cb * 16);
+        load_lds_16(Vb + off, Vt + cb * 16);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int cb = (wu * CPW + u) * 64;
+        const int idx = cb + lane;
+        const int row = idx / RC, pc = idx % RC;
+        const int lc = pc ^ swz<RC>(row);
+        const int grow = min(kv0 + row, a.Nk - 1);
+        const size_t off = (size_t)grow * ROWB + lc * 16;
+        load_lds_16(Kh + off, Kt + cb * 16);
+        load_lds_16(Vh + off, Vt + cb * 16);
+      }
     }
   };
 
@@ -259,32 +286,51 @@ fwd_kernel(FwdArgs a) {
     }
   };
 
-  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) __attribute__((always_inline)) {
+  // A step computes tile jt from (Kt, Vt) while tile jt+1 streams into
+  // (Kn, Vn). A wavefront whose 32 rows all lie above the tile skips it;
+  // tiles that cross the diagonal or the end of K/V take the masked body.
+  auto step = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Kn, char* Vn)
+                  __attribute__((always_inline)) {
+    constexpr bool GENERIC = decltype(generic_tag)::value;
     const int kv0 = jt * BC;
     if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
-    // A wavefront whose 32 rows all lie above this tile skips it; tiles that
-    // cross the diagonal or the end of K/V take the masked body.
-    const bool active = !CAUSAL || kv0 <= q0w + 31;
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
-    if (active) {
-      if (need_mask)
-        body(std::true_type{}, jt, Kt, Vt);
-      else
-        body(std::false_type{}, jt, Kt, Vt);
+    if constexpr (GENERIC) {
+      const bool active = !CAUSAL || kv0 <= q0w + 31;
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
+      if (active) {
+        if (need_mask)
+          body(std::true_type{}, jt, Kt, Vt);
+        else
+          body(std::false_type{}, jt, Kt, Vt);
+      }
+    } else {
+      body(std::false_type{}, jt, Kt, Vt);
     }
     wait_vmem();
     __syncthreads();
   };
 
+  // Q tiles start at multiples of BR (a multiple of BC), so every tile
+  // before the last BR / BC ones ends at or before the first row of the Q
+  // tile and inside K/V: it is unmasked for every wavefront, and the main
+  // loop runs the unmasked body only. The last BR / BC tiles take the
+  // generic step.
+  constexpr int NTAIL = BR / BC;
+  const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
   issue_tile(0, sK0, sV0);
   wait_vmem();
   __syncthreads();
   int jt = 0;
-  for (; jt + 1 < n_kv; jt += 2) {
-    step(jt, sK0, sV0, sK1, sV1);
-    step(jt + 1, sK1, sV1, sK0, sV0);
+  for (; jt + 1 < n_main; jt += 2) {
+    step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
+    step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
   }
-  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
+  for (; jt < n_kv; ++jt) {
+    if (jt & 1)
+      step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
+    else
+      step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+  }
 
   // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
   const float lt = half_swap_add(lsum);
