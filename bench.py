@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
+    p.add_argument("--summarize-profiles", default=None, metavar="DIR",
+                   help="summarise rocprofv3 output under DIR/{trace,fetch,write} (no GPU needed) and record "
+                        "the HBM bytes per launch for the current kernel sources")
+    p.add_argument("--calibration-mib", type=int, default=256, help="copy size used by the counter runs")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, copy a MIB-MiB buffer 3 times (a plain copy kernel of known size, to "
                         "scale the HBM byte counters of a profiler run)")
@@ -137,23 +141,131 @@ def time_calls(step, calls, steps, warmup):
     return per_step, per_call, wall
 
 
-def measured_traffic(call):
-    """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
-    have changed since they were taken."""
+def csrc_sha256():
+    """sha256 over the kernel sources (file names and contents, sorted)."""
     import hashlib
     csrc = os.path.join(ROOT, "exact_tiled_attention_28_amd", "csrc")
-    rec_path = os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
-    if not os.path.exists(rec_path):
-        return None
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         h.update(f.encode())
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    return h.hexdigest()
+
+
+# Kernels of each C entry point, by the name rocprofv3 reports (demangled,
+# or mangled for the preprocess kernel, whose last template argument says
+# whether it also zeroes dQ: only fa_bwd_atomic's does).
+CALL_KERNELS = {
+    "fa_fwd": ("void fa::fwd_kernel<", "void fa::fwd_pp_kernel<"),
+    "fa_bwd": ("void fa::bwd_dkdv_kernel<", "void fa::bwd_dq_kernel<"),
+    "fa_bwd_atomic": ("void fa::bwd_kernel<",),
+}
+
+
+def _call_of(kernel):
+    if "bwd_preprocess_kernel" in kernel:
+        zero_dq = kernel.rstrip().endswith(", true>(fa::BwdArgs)") or "Lb1EEEv" in kernel or ", true>" in kernel
+        return "fa_bwd_atomic" if zero_dq else "fa_bwd"
+    for call, prefixes in CALL_KERNELS.items():
+        if kernel.startswith(prefixes):
+            return call
+    return None
+
+
+def summarize_profiles(prof_dir, calib_mib, out_path=None):
+    """Turn the rocprofv3 output of one kernel-trace run (prof_dir/trace) and
+    two counter runs (prof_dir/fetch: FETCH_SIZE, prof_dir/write: WRITE_SIZE,
+    each with --copy-calibration calib_mib) into markdown tables, and record
+    the copy-calibrated HBM bytes per launch of fa_fwd / fa_bwd for the
+    current kernel sources in measured_traffic.json."""
+    import csv
+    import glob
+
+    def rows(sub, suffix):
+        files = glob.glob(os.path.join(prof_dir, sub, "*" + suffix))
+        if not files:
+            raise SystemExit(f"no *{suffix} under {os.path.join(prof_dir, sub)}")
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    stats = rows("trace", "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in stats)
+    print("| kernel | entry point | calls | average µs | min µs | max µs | share |")
+    print("|---|---|---|---|---|---|---|")
+    per_call_us = {}
+    for r in stats:
+        name = r["Name"]
+        call = _call_of(name)
+        avg = float(r["AverageNs"]) / 1e3
+        print(f"| `{name}` | {call or '-'} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+        if call:
+            per_call_us[call] = per_call_us.get(call, 0.0) + avg
+    print()
+    for call, us in sorted(per_call_us.items()):
+        print(f"- `{call}`: sum of its kernels' average durations {us:.1f} µs")
+    print()
+
+    counters = {}
+    for sub, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        acc = {}
+        for r in rows(sub, "counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            k = acc.setdefault(r["Kernel_Name"], {})
+            k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        counters[cname] = {name: sum(v.values()) / len(v) for name, v in acc.items()}
+    calib_kib = calib_mib * 1024
+    scale = {}
+    for cname, per in counters.items():
+        copies = [v for name, v in per.items() if "copyBuffer" in name]
+        if not copies:
+            raise SystemExit(f"{cname}: no copy kernel in the counter run (run it with --copy-calibration)")
+        scale[cname] = calib_kib / (sum(copies) / len(copies))
+    print(f"Calibration: a copy of {calib_mib} MiB reads {calib_kib / scale['FETCH_SIZE']:.0f} KiB of FETCH_SIZE "
+          f"(scale x{scale['FETCH_SIZE']:.4f}) and {calib_kib / scale['WRITE_SIZE']:.0f} KiB of WRITE_SIZE "
+          f"(scale x{scale['WRITE_SIZE']:.4f}).")
+    print()
+    print("| kernel | entry point | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) |")
+    print("|---|---|---|---|---|")
+    per_call = {}
+    names = sorted(set(counters["FETCH_SIZE"]) | set(counters["WRITE_SIZE"]))
+    for name in names:
+        call = _call_of(name)
+        if call is None:
+            continue
+        f = counters["FETCH_SIZE"].get(name, 0.0)
+        wr = counters["WRITE_SIZE"].get(name, 0.0)
+        fb, wb = f * 1024 * scale["FETCH_SIZE"], wr * 1024 * scale["WRITE_SIZE"]
+        print(f"| `{name}` | {call} | {f:.0f} | {wr:.0f} | {(fb + wb) / 1e6:.0f} |")
+        c = per_call.setdefault(call, {"fetch_bytes": 0, "write_bytes": 0})
+        c["fetch_bytes"] += int(round(fb))
+        c["write_bytes"] += int(round(wb))
+    print()
+    for call, c in sorted(per_call.items()):
+        print(f"- `{call}`: {(c['fetch_bytes'] + c['write_bytes']) / 1e6:.0f} MB per launch")
+    rec = {"note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), "
+                   "scaled by the same counters on a copy of known size",
+           "kernel_sources_sha256": csrc_sha256(), "workload": "fwd_bf16_causal_b8_h16_n2048_d128",
+           "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4)}
+    rec.update({k: v for k, v in per_call.items() if k in ("fa_fwd", "fa_bwd")})
+    out_path = out_path or os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"\nkernel sources sha256 {rec['kernel_sources_sha256']}")
+
+
+def measured_traffic(call):
+    """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
+    have changed since they were taken."""
+    rec_path = os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
+    if not os.path.exists(rec_path):
+        return None
     with open(rec_path) as fh:
         rec = json.load(fh)
-    if rec.get("kernel_sources_sha256") != h.hexdigest() or call not in rec:
+    if rec.get("kernel_sources_sha256") != csrc_sha256() or call not in rec:
         return None
     return rec[call]["fetch_bytes"] + rec[call]["write_bytes"]
 
@@ -183,6 +295,8 @@ def cpu_baseline(w, inp, heads):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles, args.calibration_mib)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the attention path runs on one GPU)", file=sys.stderr)
@@ -215,7 +329,7 @@ def main():
     avg_fwd = float(np.mean(per_call[:, 0]))
     avg_bwd = float(np.mean(per_call[:, 1]))
     if avg_bwd >= avg_fwd:
-        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_kernel + bwd_dq_kernel, one call)", "flops": bf,
+        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_dkdv_kernel + bwd_dq_kernel, one call)", "flops": bf,
                "ms": avg_bwd, "traffic": measured_traffic("fa_bwd")}
     else:
         dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd, "traffic": measured_traffic("fa_fwd")}
