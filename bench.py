@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
+    p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
                    help="summarise rocprofv3 output under DIR/{trace,fetch,write} (no GPU needed) and record "
                         "the HBM bytes per launch for the current kernel sources")
@@ -122,6 +123,7 @@ def time_calls(step, calls, steps, warmup):
     """Run `calls` (a list of callables) per step; return the step times and
     per-call times (ms) from HIP events recorded on the launch stream."""
     import torch
+    stream = step.stream if step is not None else torch.cuda.current_stream()
     for _ in range(warmup):
         for c in calls:
             c()
@@ -130,15 +132,72 @@ def time_calls(step, calls, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        ev[s][0].record(step.stream)
+        ev[s][0].record(stream)
         for i, c in enumerate(calls):
             c()
-            ev[s][i + 1].record(step.stream)
+            ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     per_call = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(calls))] for s in range(steps)])
     per_step = per_call.sum(axis=1)
     return per_step, per_call, wall
+
+
+# Packed variable-length batch timed by --varlen: 16 causal sequences whose
+# lengths are drawn uniformly from [256, 4096] (seed 11), Hq = Hkv = 16,
+# d = 128, bf16 (a mix like the unequal-length batches the FlashAttention-3
+# news page names; no dataset is involved).
+VARLEN_SEED, VARLEN_SEQS, VARLEN_MIN, VARLEN_MAX, VARLEN_H, VARLEN_D = 11, 16, 256, 4096, 16, 128
+
+
+def bench_varlen(args):
+    """Time fa_fwd_varlen + fa_bwd_varlen on the packed batch above; prints
+    one JSON line (TFLOPS on the causal-adjusted count summed over the
+    sequences)."""
+    import torch
+    from exact_tiled_attention_28_amd.inputs import make_varlen_inputs
+    rng = np.random.default_rng(VARLEN_SEED)
+    lengths = rng.integers(VARLEN_MIN, VARLEN_MAX + 1, size=VARLEN_SEQS)
+    inp = make_varlen_inputs(VARLEN_SEED, lengths, lengths, VARLEN_H, VARLEN_H, VARLEN_D, with_do=True)
+    dev = torch.device("cuda")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).bfloat16()
+    q, k, v, do = up(inp.q), up(inp.k), up(inp.v), up(inp.do)
+    cu = torch.from_numpy(inp.cu_q).to(dev)
+    H, T, d = q.shape
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((H, T, d), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(binding.fa_bwd_workspace_bytes(1, H, T) // 4, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    bf = binding.FA_DTYPE_BF16
+    B, mx = len(lengths), int(inp.max_q)
+
+    def fwd():
+        rc = binding.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   cu.data_ptr(), cu.data_ptr(), B, mx, mx, T, T, H, H, d, scale, 1, bf, bf, sh)
+        if rc:
+            raise binding.FAError(rc, "fa_fwd_varlen", binding.fa_last_error())
+
+    def bwd():
+        rc = binding.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                   cu.data_ptr(), cu.data_ptr(), B, mx, mx, T, T, H, H, d, scale, 1, bf, bf, bf, sh)
+        if rc:
+            raise binding.FAError(rc, "fa_bwd_varlen", binding.fa_last_error())
+
+    _, per_call, _ = time_calls(None, [fwd, bwd], args.steps, args.warmup)
+    fwd_ms, bwd_ms = float(np.median(per_call[:, 0])), float(np.median(per_call[:, 1]))
+    ff = sum(fwd_flops(1, H, int(n), int(n), d, True) for n in lengths)
+    bfl = sum(bwd_flops(1, H, int(n), int(n), d, True) for n in lengths)
+    out = {"workload": f"varlen causal bf16: {B} sequences, lengths U[{VARLEN_MIN},{VARLEN_MAX}] (seed {VARLEN_SEED}), "
+                       f"total {T} tokens, max {mx}, H={H}, d={d}",
+           "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
+           "bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(bfl / (bwd_ms * 1e-3) / 1e12, 2)}
+    out["fwd_pct_of_bf16_peak"] = round(100 * out["fwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 2)
+    out["bwd_pct_of_bf16_peak"] = round(100 * out["bwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 2)
+    print(json.dumps(out), flush=True)
 
 
 def csrc_sha256():
@@ -163,7 +222,21 @@ CALL_KERNELS = {
 }
 
 
+def _template_args(kernel):
+    """Template arguments of a demangled kernel name, as strings."""
+    if "<" not in kernel or ">(" not in kernel:
+        return []
+    return [t.strip() for t in kernel[kernel.index("<") + 1:kernel.rindex(">(")].split(",")]
+
+
 def _call_of(kernel):
+    t = _template_args(kernel)
+    # variable-length instances carry a trailing VARLEN = true argument
+    if ((kernel.startswith("void fa::fwd_kernel<") and len(t) == 6)
+            or (kernel.startswith("void fa::bwd_dkdv_kernel<") and len(t) == 4)
+            or (kernel.startswith("void fa::bwd_dq_kernel<") and len(t) == 3)):
+        if t[-1] == "true":
+            return "fa_fwd_varlen" if "fwd_kernel" in kernel else "fa_bwd_varlen"
     if "bwd_preprocess_kernel" in kernel:
         zero_dq = kernel.rstrip().endswith(", true>(fa::BwdArgs)") or "Lb1EEEv" in kernel or ", true>" in kernel
         return "fa_bwd_atomic" if zero_dq else "fa_bwd"
@@ -207,6 +280,8 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
         print(f"- `{call}`: sum of its kernels' average durations {us:.1f} µs")
     print()
 
+    if not os.path.isdir(os.path.join(prof_dir, "fetch")):
+        return  # a kernel-trace-only run
     counters = {}
     for sub, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
         acc = {}
@@ -309,6 +384,8 @@ def main():
 
     if args.workload:
         return bench_one(args)
+    if args.varlen:
+        return bench_varlen(args)
 
     w = WORKLOADS[STEP_WORKLOAD]
     inp, q, k, v, do = device_inputs(w, with_do=True)

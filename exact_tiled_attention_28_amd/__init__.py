@@ -14,13 +14,17 @@ from .binding import (  # noqa: F401
     FA_OK,
     FAError,
     backward,
+    backward_varlen,
     fa_bwd,
     fa_bwd_atomic,
+    fa_bwd_varlen,
     fa_bwd_workspace_bytes,
     fa_fwd,
+    fa_fwd_varlen,
     fa_last_error,
     fa_status_string,
     fa_version,
     forward,
+    forward_varlen,
     load_library,
 )

@@ -3,12 +3,14 @@ every step of the attention computation runs in the library's HIP kernels.
 
 Two levels:
 
-* ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_workspace_bytes`` / ``fa_status_string``
-  / ``fa_last_error`` / ``fa_version`` mirror the C functions one to one
+* ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_atomic`` / ``fa_fwd_varlen`` /
+  ``fa_bwd_varlen`` / ``fa_bwd_workspace_bytes`` / ``fa_status_string`` /
+  ``fa_last_error`` / ``fa_version`` mirror the C functions one to one
   (pointers and streams as Python ints);
-* ``forward`` / ``backward`` take torch tensors on the GPU, allocate the
-  outputs with torch, call the C functions on torch's current stream and
-  raise ``FAError`` on a non-zero status.
+* ``forward`` / ``backward`` / ``forward_varlen`` / ``backward_varlen`` take
+  torch tensors on the GPU, allocate the outputs with torch, call the C
+  functions on torch's current stream and raise ``FAError`` on a non-zero
+  status.
 
 There is no fallback: if the library is missing, loading it raises.
 """
@@ -57,6 +59,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for fn in (lib.fa_bwd, lib.fa_bwd_atomic):
         fn.restype = _c_int
         fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    lib.fa_fwd_varlen.restype = _c_int
+    lib.fa_fwd_varlen.argtypes = [_c_ptr] * 7 + [_c_int] * 8 + [_c_float] + [_c_int] * 3 + [_c_ptr]
+    lib.fa_bwd_varlen.restype = _c_int
+    lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -91,6 +97,21 @@ def fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads
     return load_library().fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
                                         seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
                                         stream)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads,
+                  n_kv_heads, head_dim, scale, causal, in_dtype, out_dtype, stream) -> int:
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k, total_q,
+                                        total_k, n_q_heads, n_kv_heads, head_dim, scale, causal, in_dtype, out_dtype,
+                                        stream)
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k,
+                  total_q, total_k, n_q_heads, n_kv_heads, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
+                  stream) -> int:
+    return load_library().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch,
+                                        max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim,
+                                        scale, causal, in_dtype, o_dtype, grad_dtype, stream)
 
 
 def fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q) -> int:
@@ -181,3 +202,49 @@ def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None, a
             int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
     _check(rc, fn.__name__)
     return dq, dk, dv, ws[:B * Hq * Nq].view(B, Hq, Nq)
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, scale, causal, out_dtype=None, stream=None):
+    """Packed variable-length forward. q: [Hq, total_q, d]; k, v: [Hkv, total_k, d]
+    (contiguous bf16 on the GPU); cu_q, cu_k: int32 device tensors of batch + 1
+    offsets (pass the same tensor twice for causal). Returns (o, lse) with
+    o [Hq, total_q, d] and lse [Hq, total_q]."""
+    import torch
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    oc = _dtype_code(q) if out_dtype is None else (FA_DTYPE_F32 if out_dtype == torch.float32 else FA_DTYPE_BF16)
+    o = torch.empty((Hq, total_q, d), dtype=_torch_dtype(oc), device=q.device)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, cu_q, cu_k):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu_q.data_ptr(),
+                       cu_k.data_ptr(), cu_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq,
+                       Hkv, d, float(scale), int(bool(causal)), _dtype_code(q), oc, _stream_handle(stream))
+    _check(rc, "fa_fwd_varlen")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_seqlen_q, max_seqlen_k, scale, causal, grad_dtype=None,
+                    stream=None):
+    """Packed variable-length backward (layouts as in forward_varlen).
+    Returns (dq fp32 [Hq, total_q, d], dk, dv [Hkv, total_k, d], D [Hq, total_q])."""
+    import torch
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    gc = _dtype_code(q) if grad_dtype is None else (FA_DTYPE_F32 if grad_dtype == torch.float32 else FA_DTYPE_BF16)
+    dq = torch.empty((Hq, total_q, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((Hkv, total_k, d), dtype=_torch_dtype(gc), device=q.device)
+    dv = torch.empty((Hkv, total_k, d), dtype=_torch_dtype(gc), device=q.device)
+    ws = torch.empty(max(1, fa_bwd_workspace_bytes(1, Hq, total_q) // 4), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse, do, cu_q, cu_k):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(),
+                       cu_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, d,
+                       float(scale), int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
+    _check(rc, "fa_bwd_varlen")
+    return dq, dk, dv, ws[:Hq * total_q].view(Hq, total_q)

@@ -103,6 +103,89 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, co
                     head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream, true, "fa_bwd_atomic launch");
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                  int n_q_heads, int n_kv_heads, int head_dim, float scale, int causal, int in_dtype, int out_dtype,
+                  void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_ptr(q, "q", err)) || (rc = fa::check_ptr(k, "k", err)) || (rc = fa::check_ptr(v, "v", err)) ||
+      (rc = fa::check_ptr(o, "o", err)) || (rc = fa::check_ptr(lse, "lse", err)))
+    return fail(rc, err);
+  if (!fa::valid_dtype(in_dtype) || !fa::valid_dtype(out_dtype))
+    return fail(FA_ERR_INVALID_ARGUMENT, "in_dtype and out_dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16");
+  const fa::VarlenShape s{batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim};
+  if ((rc = fa::check_varlen(cu_seqlens_q, cu_seqlens_k, s, scale, causal, err))) return fail(rc, err);
+  if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the variable-length forward takes bf16 q, k, v");
+  if (max_seqlen_q == 0) return FA_OK;  // no query rows at all
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = max_seqlen_q;
+  a.Nk = max_seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  hipError_t e = fa::launch_fwd_varlen(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  return hip_status(e, "fa_fwd_varlen launch");
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  float* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int n_q_heads,
+                  int n_kv_heads, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
+                  void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_ptr(q, "q", err)) || (rc = fa::check_ptr(k, "k", err)) || (rc = fa::check_ptr(v, "v", err)) ||
+      (rc = fa::check_ptr(o, "o", err)) || (rc = fa::check_ptr(lse, "lse", err)) ||
+      (rc = fa::check_ptr(dout, "dout", err)) || (rc = fa::check_ptr(dq, "dq", err)) ||
+      (rc = fa::check_ptr(dk, "dk", err)) || (rc = fa::check_ptr(dv, "dv", err)) ||
+      (rc = fa::check_ptr(workspace, "workspace", err)))
+    return fail(rc, err);
+  if (!fa::valid_dtype(in_dtype) || !fa::valid_dtype(o_dtype) || !fa::valid_dtype(grad_dtype))
+    return fail(FA_ERR_INVALID_ARGUMENT, "dtypes must be FA_DTYPE_F32 or FA_DTYPE_BF16");
+  const fa::VarlenShape s{batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim};
+  if ((rc = fa::check_varlen(cu_seqlens_q, cu_seqlens_k, s, scale, causal, err))) return fail(rc, err);
+  if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes bf16 q, k, v, dout");
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dvec = workspace;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = max_seqlen_q;
+  a.Nk = max_seqlen_k;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  hipError_t e = fa::launch_bwd_varlen(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
+                                       (hipStream_t)stream);
+  return hip_status(e, "fa_bwd_varlen launch");
+}
+
 size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q) {
   if (batch <= 0 || n_q_heads <= 0 || seqlen_q <= 0) return 0;
   return (size_t)4 * (size_t)batch * (size_t)n_q_heads * (size_t)seqlen_q;

@@ -111,4 +111,68 @@ inline int check_bwd(const void* q, const void* k, const void* v, const void* o,
   return FA_OK;
 }
 
+// Packed variable-length batch (fa_fwd_varlen / fa_bwd_varlen).
+struct VarlenShape {
+  int batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim;
+};
+
+inline int check_varlen(const void* cu_q, const void* cu_k, const VarlenShape& s, float scale, int causal,
+                        std::string& err) {
+  char buf[256];
+  if (cu_q == nullptr || cu_k == nullptr) {
+    err = cu_q == nullptr ? "cu_seqlens_q is NULL" : "cu_seqlens_k is NULL";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if ((reinterpret_cast<uintptr_t>(cu_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_k) & 3u)) {
+    err = "cu_seqlens_q / cu_seqlens_k must be 4-byte aligned";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (s.batch < 1 || s.n_q_heads < 1 || s.n_kv_heads < 1) {
+    std::snprintf(buf, sizeof buf, "batch, n_q_heads and n_kv_heads must be >= 1 (got %d, %d, %d)", s.batch,
+                  s.n_q_heads, s.n_kv_heads);
+    err = buf;
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (s.max_seqlen_q < 0 || s.max_seqlen_k < 0 || s.total_q < 0 || s.total_k < 0 || s.max_seqlen_q > s.total_q ||
+      s.max_seqlen_k > s.total_k) {
+    std::snprintf(buf, sizeof buf,
+                  "need 0 <= max_seqlen <= total (got max_seqlen_q=%d total_q=%d max_seqlen_k=%d total_k=%d)",
+                  s.max_seqlen_q, s.total_q, s.max_seqlen_k, s.total_k);
+    err = buf;
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (s.n_q_heads % s.n_kv_heads != 0) {
+    std::snprintf(buf, sizeof buf, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", s.n_q_heads, s.n_kv_heads);
+    err = buf;
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (causal != 0 && causal != 1) {
+    err = "causal must be 0 or 1";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(scale)) {
+    err = "scale must be finite";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (s.head_dim != 64 && s.head_dim != 128) {
+    std::snprintf(buf, sizeof buf, "head_dim %d unsupported (64 or 128)", s.head_dim);
+    err = buf;
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (causal && (cu_q != cu_k || s.max_seqlen_q != s.max_seqlen_k || s.total_q != s.total_k)) {
+    err = "causal attention needs the same sequences for queries and keys (cu_seqlens_q == cu_seqlens_k, equal "
+          "max_seqlen and total)";
+    return FA_ERR_UNSUPPORTED;
+  }
+  if ((long long)s.total_q * s.head_dim >= (1LL << 31) || (long long)s.total_k * s.head_dim >= (1LL << 31)) {
+    err = "total * head_dim must be below 2^31";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if ((long long)s.batch * s.n_q_heads >= (1LL << 31) / 1024) {
+    err = "batch * n_q_heads too large";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  return FA_OK;
+}
+
 }  // namespace fa

@@ -437,7 +437,7 @@ struct DkdvTile {
   static_assert(RED_BYTES <= 4 * QTILEB, "the reduction buffer reuses the Q / dO tiles");
 };
 
-template <int D, bool CAUSAL, bool GF32>
+template <int D, bool CAUSAL, bool GF32, bool VARLEN = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D>;
   constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB;
@@ -467,7 +467,27 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kv0 = ui.item * BKV;
   const int key = kv0 + 32 * kg + l32;  // this lane's key
 
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  // Sequence lengths and head bases: fixed-length [B][H][N][d], or a packed
+  // variable-length batch [H][total][d] (a.Nq / a.Nk are then the longest
+  // lengths); q_base(hq) is the first row of query head hq of this sequence.
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t kvhead;
+  int q_off = 0;
+  if constexpr (VARLEN) {
+    const SeqSpan sq = clamp_span(a.cu_q[b], a.cu_q[b + 1], a.total_q, a.Nq);
+    const SeqSpan sk = clamp_span(a.cu_k[b], a.cu_k[b + 1], a.total_k, a.Nk);
+    Nq = sq.len;
+    Nk = sk.len;
+    if (kv0 >= Nk) return;  // the whole key block lies past this sequence
+    q_off = sq.off;
+    kvhead = (size_t)hkv * a.total_k + sk.off;
+  } else {
+    kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  }
+  auto q_base = [&](int hq) __attribute__((always_inline)) -> size_t {
+    if constexpr (VARLEN) return (size_t)hq * a.total_q + q_off;
+    return (size_t)(b * a.Hq + hq) * a.Nq;
+  };
   const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
   const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
 
@@ -477,7 +497,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int ci = tid + 64 * T::NW * u;
     const int row = ci / RC, cc = ci % RC;
     u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (kv0 + row < a.Nk) {
+    if (kv0 + row < Nk) {
       const size_t off = (size_t)(kv0 + row) * ROWB + cc * 16;
       x = *(const u32x4*)(Kh + off);
       y = *(const u32x4*)(Vh + off);
@@ -505,7 +525,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     dvacc[db] = f32x16{};
   }
 
-  const int n_qblk = ceil_div(a.Nq, BQ);
+  const int n_qblk = ceil_div(Nq, BQ);
   const int i_first = first_q_tile_for(kv0, BQ, CAUSAL);
   const int n_i = n_qblk - i_first;
   const int total = a.G * n_i;
@@ -517,7 +537,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int hm = it / n_i;
     const int i = i_first + it % n_i;
     const int hq = hkv * a.G + hm;
-    const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    const size_t qhead = q_base(hq);
     const int q0 = i * BQ;
     const char* Qh = (const char*)a.q + qhead * ROWB;
     const char* Oh = (const char*)a.dout + qhead * ROWB;
@@ -527,12 +547,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int idx = cb + lane;
       const int row = idx / RC, pc = idx % RC;
       const int lc = pc ^ swz<RC>(row);
-      const size_t off = (size_t)min(q0 + row, a.Nq - 1) * ROWB + lc * 16;
+      const size_t off = (size_t)min(q0 + row, Nq - 1) * ROWB + lc * 16;
       load_lds_16(Qh + off, sQ + buf * QTILEB + cb * 16);
       load_lds_16(Oh + off, sDO + buf * QTILEB + cb * 16);
     }
     if (tid < BQ) {
-      const bool ok = q0 + tid < a.Nq;
+      const bool ok = q0 + tid < Nq;
       lr = ok ? a.lse[qhead + q0 + tid] * kLog2e : INFINITY;
       dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
     }
@@ -573,7 +593,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int e = 0; e < 4; ++e) {
         float p = fast_exp2(fmaf(s[4 * a4 + e], c, -lv[e]));
         if constexpr (MASK) {
-          const bool vis = key < a.Nk && (!CAUSAL || key <= q0 + r0 + e);
+          const bool vis = key < Nk && (!CAUSAL || key <= q0 + r0 + e);
           p = vis ? p : 0.0f;
         }
         s[4 * a4 + e] = p;
@@ -641,7 +661,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Skip when all of this wavefront's keys lie after all of its queries.
     const bool active = !CAUSAL || kv0 + 32 * kg <= q0 + 32 * qh + 31;
     if (active) {
-      const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * qh) || (kv0 + 32 * kg + 32 > a.Nk);
+      const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * qh) || (kv0 + 32 * kg + 32 > Nk);
       if (need_mask)
         body(std::true_type{}, q0, tQ, tDO, tL, tD);
       else
@@ -679,7 +699,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   exchange(dkacc);
   exchange(dvacc);
 
-  if (qh == 0 && key < a.Nk) {
+  if (qh == 0 && key < Nk) {
     const size_t rowoff = (kvhead + key) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -712,7 +732,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 // S^T = K Q^T and dP^T = V dO^T take Q and dO as register B operands, L and D
 // are per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from the
 // accumulator registers and K^T by transpose reads of the K tile.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 4, BR = 32 * NW, BC = 64, NKB = BC / 32;
   constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB, CPW = TILEB / (1024 * NW);
@@ -742,8 +762,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int q0w = q0 + 32 * w;
   const int qrow = q0w + l32;
 
-  const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  // Fixed-length [B][H][N][d], or a packed variable-length batch [H][total][d]
+  // (a.Nq / a.Nk are then the longest lengths).
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t qhead, kvhead;
+  if constexpr (VARLEN) {
+    const SeqSpan sq = clamp_span(a.cu_q[b], a.cu_q[b + 1], a.total_q, a.Nq);
+    const SeqSpan sk = clamp_span(a.cu_k[b], a.cu_k[b + 1], a.total_k, a.Nk);
+    Nq = sq.len;
+    Nk = sk.len;
+    if (q0 >= Nq) return;  // the whole Q tile lies past this sequence
+    qhead = (size_t)hq * a.total_q + sq.off;
+    kvhead = (size_t)hkv * a.total_k + sk.off;
+  } else {
+    qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  }
   const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
   const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
 
@@ -754,7 +788,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (qrow < a.Nq) {
+      if (qrow < Nq) {
         x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
         y = *(const u32x4*)(Or + (kk * 16 + 8 * g) * 2);
       }
@@ -763,10 +797,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   // Rows past the end get L = +inf, so their P (and dS) is 0.
-  const float l2 = qrow < a.Nq ? a.lse[qhead + qrow] * kLog2e : INFINITY;
-  const float dq_d = qrow < a.Nq ? a.dvec[qhead + qrow] : 0.0f;
+  const float l2 = qrow < Nq ? a.lse[qhead + qrow] * kLog2e : INFINITY;
+  const float dq_d = qrow < Nq ? a.dvec[qhead + qrow] : 0.0f;
 
-  const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
+  const int kv_end = kv_end_for(q0, BR, Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
   // This lane's 16-byte chunk of wave load u of a K/V tile, as a byte offset
@@ -786,7 +820,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
-    if (kv0 + BC <= a.Nk) {
+    if (kv0 + BC <= Nk) {
       const char* Kb = Kh + (size_t)kv0 * ROWB;
       const char* Vb = Vh + (size_t)kv0 * ROWB;
 #pragma unroll
@@ -803,7 +837,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int idx = cb + lane;
         const int row = idx / RC, pc = idx % RC;
         const int lc = pc ^ swz<RC>(row);
-        const size_t off = (size_t)min(kv0 + row, a.Nk - 1) * ROWB + lc * 16;
+        const size_t off = (size_t)min(kv0 + row, Nk - 1) * ROWB + lc * 16;
         load_lds_16(Kh + off, Kt + cb * 16);
         load_lds_16(Vh + off, Vt + cb * 16);
       }
@@ -846,7 +880,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         float p = fast_exp2(fmaf(sacc[r], c, -l2));
         if constexpr (MASK) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
+          const bool vis = key < Nk && (!CAUSAL || key <= qrow);
           p = vis ? p : 0.0f;
         }
         dsv[r] = p * (dpacc[r] - dq_d);
@@ -870,32 +904,51 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) __attribute__((always_inline)) {
+  // A step computes tile jt while tile jt+1 streams in. The generic step
+  // skips tiles entirely above a wavefront's rows and masks tiles that cross
+  // the diagonal or the end of K/V; as in the forward, every tile before the
+  // last BR / BC ones is unmasked for every wavefront (Q tiles start at
+  // multiples of BR), so the main loop runs the unmasked body only.
+  auto step = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Kn, char* Vn)
+                  __attribute__((always_inline)) {
+    constexpr bool GENERIC = decltype(generic_tag)::value;
     const int kv0 = jt * BC;
     if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
-    const bool active = !CAUSAL || kv0 <= q0w + 31;
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
-    if (active) {
-      if (need_mask)
-        body(std::true_type{}, jt, Kt, Vt);
-      else
-        body(std::false_type{}, jt, Kt, Vt);
+    if constexpr (GENERIC) {
+      const bool active = !CAUSAL || kv0 <= q0w + 31;
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > Nk);
+      if (active) {
+        if (need_mask)
+          body(std::true_type{}, jt, Kt, Vt);
+        else
+          body(std::false_type{}, jt, Kt, Vt);
+      }
+    } else {
+      body(std::false_type{}, jt, Kt, Vt);
     }
     wait_vmem();
     __syncthreads();
   };
 
-  issue_tile(0, sK0, sV0);
+  constexpr int NTAIL = BR / BC;
+  const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
+  // A sequence with no keys (variable-length batches only) has dQ = 0.
+  if (n_kv > 0) issue_tile(0, sK0, sV0);
   wait_vmem();
   __syncthreads();
   int jt = 0;
-  for (; jt + 1 < n_kv; jt += 2) {
-    step(jt, sK0, sV0, sK1, sV1);
-    step(jt + 1, sK1, sV1, sK0, sV0);
+  for (; jt + 1 < n_main; jt += 2) {
+    step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
+    step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
   }
-  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
+  for (; jt < n_kv; ++jt) {
+    if (jt & 1)
+      step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
+    else
+      step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+  }
 
-  if (qrow < a.Nq) {
+  if (qrow < Nq) {
     float* dqr = a.dq + (qhead + qrow) * D;
     const float scale = a.scale;
 #pragma unroll
@@ -962,6 +1015,51 @@ static hipError_t launch_bwd_all(const BwdArgs& a, bool o_f32, bool atomic_dq, h
   e = launch_bwd_dkdv<D, CAUSAL, GF32>(a, s);
   if (e != hipSuccess) return e;
   return launch_bwd_dq<D, CAUSAL>(a, s);
+}
+
+// Packed variable-length batch: the D preprocess runs over the Hq x total_q
+// rows as one flat array; the dK/dV and dQ grids cover the longest sequence
+// and workgroups past their sequence's end exit at once.
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_varlen_t(const BwdArgs& a, bool o_f32, hipStream_t s) {
+  const long long rows = (long long)a.Hq * a.total_q;
+  const long long threads = rows * (D / 8);
+  const unsigned pblocks = (unsigned)((threads + 255) / 256);
+  const __bf16* dout = (const __bf16*)a.dout;
+  if (pblocks > 0) {
+    if (o_f32)
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+    else
+      hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    using T = DkdvTile<D>;
+    auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
+    if (blocks > 0) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), T::LDS_BYTES, s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
+  if (blocks > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
+  if (head_dim == 64) {
+    if (causal)
+      return grad_f32 ? launch_bwd_varlen_t<64, true, true>(a, o_f32, s) : launch_bwd_varlen_t<64, true, false>(a, o_f32, s);
+    return grad_f32 ? launch_bwd_varlen_t<64, false, true>(a, o_f32, s) : launch_bwd_varlen_t<64, false, false>(a, o_f32, s);
+  }
+  if (causal)
+    return grad_f32 ? launch_bwd_varlen_t<128, true, true>(a, o_f32, s) : launch_bwd_varlen_t<128, true, false>(a, o_f32, s);
+  return grad_f32 ? launch_bwd_varlen_t<128, false, true>(a, o_f32, s) : launch_bwd_varlen_t<128, false, false>(a, o_f32, s);
 }
 
 template <int D>

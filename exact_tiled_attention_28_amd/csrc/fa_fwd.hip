@@ -55,7 +55,7 @@ struct FwdTile {
 // the largest probability of a row is exactly 1 (no bf16 rounding on it),
 // as in the eager rescale.
 
-template <bool F32IN, int D, bool CAUSAL, bool OUTF32, int NW>
+template <bool F32IN, int D, bool CAUSAL, bool OUTF32, int NW, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(F32IN ? 1 : 2, F32IN ? 1 : 2)))
 fwd_kernel(FwdArgs a) {
   using T = FwdTile<F32IN, D, NW>;
@@ -89,8 +89,37 @@ fwd_kernel(FwdArgs a) {
   const int q0w = q0 + 32 * w;
   const int qrow = q0w + l32;
 
-  const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  // Sequence lengths and head bases: fixed-length [B][H][N][d], or a packed
+  // variable-length batch [H][total][d] with sequence b at rows
+  // [cu[b], cu[b + 1]) (then a.Nq / a.Nk are the longest lengths).
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t qhead, kvhead;
+  if constexpr (VARLEN) {
+    const SeqSpan sq = clamp_span(a.cu_q[b], a.cu_q[b + 1], a.total_q, a.Nq);
+    const SeqSpan sk = clamp_span(a.cu_k[b], a.cu_k[b + 1], a.total_k, a.Nk);
+    Nq = sq.len;
+    Nk = sk.len;
+    if (q0 >= Nq) return;  // the whole Q tile lies past this sequence
+    qhead = (size_t)hq * a.total_q + sq.off;
+    kvhead = (size_t)hkv * a.total_k + sk.off;
+    if (Nk == 0) {
+      // No keys: O = 0 and L = -inf (logsumexp of an empty set).
+      if (qrow < Nq) {
+#pragma unroll
+        for (int d0 = 4 * g; d0 < D; d0 += 8) {
+          if constexpr (OUTF32)
+            *(f32x4*)((float*)a.o + (qhead + qrow) * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+          else
+            *(bf16x4*)((__bf16*)a.o + (qhead + qrow) * D + d0) = bf16x4{};
+        }
+        if (g == 0) a.lse[qhead + qrow] = -INFINITY;
+      }
+      return;
+    }
+  } else {
+    qhead = (size_t)(b * a.Hq + hq) * a.Nq;
+    kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  }
   const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
   const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
 
@@ -101,7 +130,7 @@ fwd_kernel(FwdArgs a) {
   if constexpr (F32IN) {
     const float* Qr = (const float*)a.q + (qhead + qrow) * D;
     for (int kk = 0; kk < NQF; ++kk) {
-      float x = (qrow < a.Nq) ? Qr[2 * kk + g] : 0.0f;
+      float x = (qrow < Nq) ? Qr[2 * kk + g] : 0.0f;
       qf[kk] = a.neg ? -x : x;
     }
   } else {
@@ -109,13 +138,13 @@ fwd_kernel(FwdArgs a) {
     const unsigned sign = a.neg ? 0x80008000u : 0u;
     for (int kk = 0; kk < NQF; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < a.Nq) x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
+      if (qrow < Nq) x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
       x ^= sign;
       qf[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
+  const int kv_end = kv_end_for(q0, BR, Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
   // ---- K/V tile staging: HBM -> swizzled LDS, no registers ------------------
@@ -138,7 +167,7 @@ fwd_kernel(FwdArgs a) {
   }
   auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
-    if (kv0 + BC <= a.Nk) {
+    if (kv0 + BC <= Nk) {
       const char* Kb = Kh + (size_t)kv0 * ROWB;
       const char* Vb = Vh + (size_t)kv0 * ROWB;
 #pragma unroll
@@ -155,7 +184,7 @@ fwd_kernel(FwdArgs a) {
         const int idx = cb + lane;
         const int row = idx / RC, pc = idx % RC;
         const int lc = pc ^ swz<RC>(row);
-        const int grow = min(kv0 + row, a.Nk - 1);
+        const int grow = min(kv0 + row, Nk - 1);
         const size_t off = (size_t)grow * ROWB + lc * 16;
         load_lds_16(Kh + off, Kt + cb * 16);
         load_lds_16(Vh + off, Vt + cb * 16);
@@ -219,7 +248,7 @@ fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
+          const bool vis = key < Nk && (!CAUSAL || key <= qrow);
           sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
         }
     }
@@ -296,7 +325,7 @@ fwd_kernel(FwdArgs a) {
     if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
     if constexpr (GENERIC) {
       const bool active = !CAUSAL || kv0 <= q0w + 31;
-      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
+      const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > Nk);
       if (active) {
         if (need_mask)
           body(std::true_type{}, jt, Kt, Vt);
@@ -335,7 +364,7 @@ fwd_kernel(FwdArgs a) {
   // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
   const float lt = half_swap_add(lsum);
   const float inv = 1.0f / lt;
-  if (qrow < a.Nq) {
+  if (qrow < Nq) {
     const size_t orow = (qhead + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -637,6 +666,27 @@ static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
   const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
   hipLaunchKernelGGL((fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW>), dim3((unsigned)blocks), dim3(T::NT), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool OUTF32>
+static hipError_t launch_fwd_varlen_t(FwdArgs a, hipStream_t stream) {
+  constexpr int NW = 4;
+  using T = FwdTile<false, D, NW>;
+  a.n_q_tiles = ceil_div(a.Nq, T::BR);
+  const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_kernel<false, D, CAUSAL, OUTF32, NW, true>), dim3((unsigned)blocks), dim3(T::NT), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_varlen(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s) {
+  if (head_dim == 64) {
+    if (causal) return out_f32 ? launch_fwd_varlen_t<64, true, true>(a, s) : launch_fwd_varlen_t<64, true, false>(a, s);
+    return out_f32 ? launch_fwd_varlen_t<64, false, true>(a, s) : launch_fwd_varlen_t<64, false, false>(a, s);
+  }
+  if (causal) return out_f32 ? launch_fwd_varlen_t<128, true, true>(a, s) : launch_fwd_varlen_t<128, true, false>(a, s);
+  return out_f32 ? launch_fwd_varlen_t<128, false, true>(a, s) : launch_fwd_varlen_t<128, false, false>(a, s);
 }
 
 template <bool F32IN, int D>

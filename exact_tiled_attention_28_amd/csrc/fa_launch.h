@@ -16,6 +16,12 @@ struct FwdArgs {
   float c;        // |scale| * log2(e): scores are scaled in base 2
   int neg;        // scale < 0: Q is negated as it is loaded
   int n_q_tiles;  // filled in by the launcher
+  // Packed variable-length batch (fa_fwd_varlen): per-sequence cumulative
+  // row offsets [B + 1]; Nq / Nk then hold the maximum sequence lengths and
+  // total_q / total_k the packed row counts. Unused by fa_fwd.
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 struct BwdArgs {
@@ -32,10 +38,16 @@ struct BwdArgs {
   int B, Hq, Hkv, G, Nq, Nk;
   float scale;
   float c;  // scale * log2(e)
+  // Packed variable-length batch (fa_bwd_varlen), as in FwdArgs.
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool in_f32, bool causal, bool out_f32, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
                       hipStream_t s);
+hipError_t launch_fwd_varlen(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
+hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s);
 
 }  // namespace fa

@@ -45,6 +45,20 @@ constexpr int first_q_tile_for(int k0, int br, bool causal) { return causal ? k0
 // round-robin over the 8 XCDs of an MI355X (WG L runs on XCD L % 8), so when
 // the number of units is a multiple of 8 every workgroup of a unit runs on
 // XCD unit % 8 and the unit's K/V stays in that XCD's L2.
+// One sequence of a packed variable-length batch: rows [off, off + len) of
+// the packed arrays. Built from the caller's cumulative offsets lo = cu[b],
+// hi = cu[b + 1], clamped so that a malformed offset array can only give
+// wrong rows, never an access outside [0, total) or a length above max_len.
+struct SeqSpan {
+  int off, len;
+};
+constexpr SeqSpan clamp_span(int lo, int hi, int total, int max_len) {
+  const int o = lo < 0 ? 0 : (lo > total ? total : lo);
+  const int e = hi < o ? o : (hi > total ? total : hi);
+  const int n = e - o;
+  return SeqSpan{o, n < max_len ? n : max_len};
+}
+
 struct UnitItem {
   int unit, item;
 };

@@ -17,6 +17,10 @@ Recipe (the same for every workload):
 * bfloat16 workloads round every float32 value once, round-to-nearest-even.
 
 Layouts are row-major: Q, dO are [B, Hq, Nq, d]; K, V are [B, Hkv, Nk, d].
+
+Packed variable-length batches (``make_varlen_inputs``) draw Q, K, V, dO the
+same way with shapes [Hq, total_q, d] / [Hkv, total_k, d], where sequence b
+owns rows cu[b]..cu[b+1]-1 and cu is the running sum of the given lengths.
 """
 
 from __future__ import annotations
@@ -100,3 +104,41 @@ def make_inputs(
     else:
         dov, dob = None, None
     return AttentionInputs(qv, kv, vv, dov, dtype, qb, kb, vb, dob, channels)
+
+
+@dataclass
+class VarlenInputs:
+    """Host copies of a packed variable-length batch: ``q``, ``do``
+    [Hq, total_q, d], ``k``, ``v`` [Hkv, total_k, d] (float32 holding
+    bfloat16 values), the int32 offsets ``cu_q``, ``cu_k`` [batch + 1] and the
+    longest lengths."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray | None
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    max_q: int
+    max_k: int
+
+
+def make_varlen_inputs(seed: int, lengths_q, lengths_k, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                       with_do: bool = False) -> VarlenInputs:
+    """Draw a packed batch with the given per-sequence lengths (bf16 values)."""
+    lq = np.asarray(lengths_q, dtype=np.int64)
+    lk = np.asarray(lengths_k, dtype=np.int64)
+    if lq.shape != lk.shape or lq.ndim != 1 or np.any(lq < 0) or np.any(lk < 0):
+        raise ValueError("lengths must be two equal-size lists of non-negative integers")
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = rng.standard_normal((n_q_heads, tq, head_dim), dtype=np.float32)
+    k = rng.standard_normal((n_kv_heads, tk, head_dim), dtype=np.float32)
+    v = rng.standard_normal((n_kv_heads, tk, head_dim), dtype=np.float32)
+    do = rng.standard_normal((n_q_heads, tq, head_dim), dtype=np.float32) if with_do else None
+    q, k, v = round_to_bf16(q)[0], round_to_bf16(k)[0], round_to_bf16(v)[0]
+    if do is not None:
+        do = round_to_bf16(do)[0]
+    return VarlenInputs(q, k, v, do, cu_q, cu_k, int(lq.max(initial=0)), int(lk.max(initial=0)))

@@ -134,6 +134,54 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
                   float scale, int causal, int in_dtype, int o_dtype,
                   int grad_dtype, void* stream);
 
+/*
+ * fa_fwd_varlen — fa_fwd on a packed batch of sequences of different lengths
+ * (the variable-length batches named on the FlashAttention-3 news page among
+ * its next steps): sequence b's queries are rows [cu_seqlens_q[b],
+ * cu_seqlens_q[b+1]) of the packed query arrays and its keys rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of the packed key arrays; each
+ * sequence is attended on its own, exactly as fa_fwd with batch 1 would.
+ *
+ *   q, o     [Hq][total_q][d] (o in out_dtype), packed by head then row
+ *   k, v     [Hkv][total_k][d]
+ *   lse      [Hq][total_q] fp32
+ *   cu_seqlens_q, cu_seqlens_k  device int32 arrays of batch + 1
+ *            non-decreasing offsets, cu[0] = 0, cu[batch] = total; read
+ *            only. Offsets are clamped to [0, total] and lengths to
+ *            max_seqlen, so malformed arrays give wrong rows but no access
+ *            outside the packed arrays.
+ *   max_seqlen_q, max_seqlen_k  at least every sequence's length (0 allowed)
+ *   in_dtype must be FA_DTYPE_BF16.
+ *   causal: token i of a sequence sees that sequence's keys 0..i; requires
+ *            the same sequences for queries and keys (cu_seqlens_q ==
+ *            cu_seqlens_k as pointers, equal max_seqlen and total), else
+ *            FA_ERR_UNSUPPORTED.
+ * A sequence with queries but no keys gets O = 0 and L = -inf. Other
+ * arguments, ownership and errors as in fa_fwd.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                  int total_k, int n_q_heads, int n_kv_heads, int head_dim,
+                  float scale, int causal, int in_dtype, int out_dtype,
+                  void* stream);
+
+/*
+ * fa_bwd_varlen — fa_bwd (two passes, no atomics) on a packed batch laid out
+ * as in fa_fwd_varlen: dq [Hq][total_q][d] fp32; dk, dv [Hkv][total_k][d]
+ * grad_dtype; o, dout [Hq][total_q][d]; lse [Hq][total_q]; workspace of at
+ * least fa_bwd_workspace_bytes(1, n_q_heads, total_q) bytes, holding D as
+ * fp32 [Hq][total_q] on return. dq, dk and dv are fully overwritten (keys of
+ * a sequence without queries get dK = dV = 0; queries without keys dQ = 0).
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, float* dq, void* dk,
+                  void* dv, float* workspace, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int batch, int max_seqlen_q,
+                  int max_seqlen_k, int total_q, int total_k, int n_q_heads,
+                  int n_kv_heads, int head_dim, float scale, int causal,
+                  int in_dtype, int o_dtype, int grad_dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd and fa_bwd_atomic need: 4 * batch * n_q_heads * seqlen_q
  * (the fp32 vector D, page 6.2 section 7.3). Returns 0 for non-positive
  * arguments. */

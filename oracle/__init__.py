@@ -7,8 +7,10 @@ CPU-baseline leg of the benchmark, never by the library itself.
 from .attention import (  # noqa: F401
     backward,
     backward_head,
+    backward_varlen,
     forward,
     forward_head,
+    forward_varlen,
     probabilities_head,
     row_dot,
 )

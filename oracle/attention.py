@@ -182,3 +182,68 @@ def probabilities_head(qh, kh, scale, causal):
     m = S.max(axis=1)
     L = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     return np.exp(S - L[:, None])
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length batches
+# ---------------------------------------------------------------------------
+#
+# A batch of sequences of different lengths packed along the row axis (the
+# variable-length batches of the FlashAttention-3 news page): sequence b owns
+# query rows cu_q[b]..cu_q[b+1]-1 and key rows cu_k[b]..cu_k[b+1]-1, and
+# each sequence is attended on its own with the definition above. Arrays are
+# [H, total, d] (L: [H, total]). Reading where the pages are silent: a
+# sequence with queries but no keys has no softmax at all; its rows get
+# O = 0, L = -inf (the logsumexp of an empty set) and dQ = 0.
+
+def _spans(cu):
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing offsets starting at 0")
+    return [(int(cu[b]), int(cu[b + 1])) for b in range(cu.size - 1)]
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal):
+    """q: [Hq, total_q, d]; k, v: [Hkv, total_k, d]. Returns (O, L) float64."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    Hq, Hkv = q.shape[0], k.shape[0]
+    if Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    G = Hq // Hkv
+    sq, sk = _spans(cu_q), _spans(cu_k)
+    if len(sq) != len(sk):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must describe the same number of sequences")
+    O = np.zeros(q.shape)
+    L = np.full(q.shape[:2], _NEG_INF)
+    for (q0, q1), (k0, k1) in zip(sq, sk):
+        if q1 == q0 or k1 == k0:
+            continue
+        if causal and q1 - q0 != k1 - k0:
+            raise ValueError("causal attention needs equal query and key lengths per sequence")
+        for h in range(Hq):
+            O[h, q0:q1], L[h, q0:q1] = forward_head(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], scale, causal)
+    return O, L
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal):
+    """Gradients of forward_varlen. Returns (dQ, dK, dV) float64; dK, dV are
+    summed over the query heads sharing each K/V head."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    Hq, Hkv = q.shape[0], k.shape[0]
+    G = Hq // Hkv
+    sq, sk = _spans(cu_q), _spans(cu_k)
+    dQ = np.zeros(q.shape)
+    dK = np.zeros(k.shape)
+    dV = np.zeros(v.shape)
+    for (q0, q1), (k0, k1) in zip(sq, sk):
+        if q1 == q0 or k1 == k0:
+            continue
+        if causal and q1 - q0 != k1 - k0:
+            raise ValueError("causal attention needs equal query and key lengths per sequence")
+        for h in range(Hq):
+            g = h // G
+            dq, dk, dv = backward_head(q[h, q0:q1], k[g, k0:k1], v[g, k0:k1], do[h, q0:q1], scale, causal)
+            dQ[h, q0:q1] = dq
+            dK[g, k0:k1] += dk
+            dV[g, k0:k1] += dv
+    return dQ, dK, dV

@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_workspace_bytes", "fa_fwd", "fa_last_error", "fa_status_string",
-         "fa_version"])
+        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_varlen",
+         "fa_last_error", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -134,6 +134,66 @@ def test_bwd_argument_errors(lib, kw, code, text):
     assert text in binding.fa_last_error()
 
 
+CU = 0x20000       # fake 4-byte-aligned offset arrays
+CU2 = 0x20010
+CU_MIS = 0x20002
+
+
+def fwd_varlen(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, cu_q=CU, cu_k=CU, batch=2, max_q=16, max_k=16, total_q=20, total_k=20,
+                n_q_heads=2, n_kv_heads=1, head_dim=64, scale=0.125, causal=0, in_dtype=1, out_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_fwd_varlen(*args.values())
+
+
+def bwd_varlen(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, cu_q=CU, cu_k=CU, batch=2, max_q=16,
+                max_k=16, total_q=20, total_k=20, n_q_heads=2, n_kv_heads=1, head_dim=64, scale=0.125, causal=0,
+                in_dtype=1, o_dtype=1, grad_dtype=1, stream=None)
+    if "out_dtype" in kw:
+        kw = dict(kw)
+        kw["grad_dtype"] = kw.pop("out_dtype")
+    args.update(kw)
+    return binding.fa_bwd_varlen(*args.values())
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(cu_q=0), INVALID, "cu_seqlens_q is NULL"),
+    (dict(cu_k=0), INVALID, "cu_seqlens_k is NULL"),
+    (dict(cu_k=CU_MIS), INVALID, "4-byte aligned"),
+    (dict(batch=0), INVALID, "must be >= 1"),
+    (dict(max_q=-1), INVALID, "max_seqlen <= total"),
+    (dict(max_k=21), INVALID, "max_seqlen <= total"),
+    (dict(n_q_heads=3, n_kv_heads=2), INVALID, "multiple of n_kv_heads"),
+    (dict(causal=3), INVALID, "causal must be 0 or 1"),
+    (dict(scale=float("nan")), INVALID, "scale must be finite"),
+    (dict(head_dim=80), UNSUP, "head_dim 80"),
+    (dict(in_dtype=0), UNSUP, "bf16"),
+    (dict(out_dtype=4), INVALID, "FA_DTYPE"),
+    (dict(causal=1, cu_k=CU2), UNSUP, "same sequences"),
+    (dict(causal=1, max_k=15), UNSUP, "same sequences"),
+    (dict(total_q=1 << 25, max_q=16, head_dim=128), INVALID, "below 2^31"),
+])
+def test_varlen_argument_errors(lib, kw, code, text):
+    assert fwd_varlen(**kw) == code
+    assert text in binding.fa_last_error()
+    assert bwd_varlen(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+def test_varlen_backward_pointer_errors(lib):
+    assert bwd_varlen(dout=0) == INVALID and "dout is NULL" in binding.fa_last_error()
+    assert bwd_varlen(ws=0) == INVALID and "workspace is NULL" in binding.fa_last_error()
+    assert bwd_varlen(dq=MIS) == INVALID and "dq is not 16-byte aligned" in binding.fa_last_error()
+
+
+def test_varlen_without_query_rows_launches_nothing(lib):
+    # max_seqlen_q == 0: nothing to compute; the call succeeds without a GPU
+    # launch (the fake pointers are never touched).
+    assert fwd_varlen(max_q=0, total_q=0) == 0
+
+
 def test_errors_are_thread_local(lib):
     import threading
     assert fwd(q=0) == INVALID
@@ -167,6 +227,13 @@ int main() {
         for (int q0 = 0; q0 < n; q0 += br)
           std::printf("K %d %d %d %d %d %d %d\n", n, br, bc, q0, fa::kv_tiles_for(q0, br, n, bc, true),
                       fa::kv_tiles_for(q0, br, n, bc, false), fa::first_q_tile_for(q0, br, true));
+  for (int lo = -3; lo <= 12; ++lo)
+    for (int hi = -3; hi <= 12; ++hi)
+      for (int total = 0; total <= 9; total += 3)
+        for (int mx = 0; mx <= 10; mx += 5) {
+          fa::SeqSpan sp = fa::clamp_span(lo, hi, total, mx);
+          std::printf("S %d %d %d %d %d %d\n", lo, hi, total, mx, sp.off, sp.len);
+        }
   for (int units = 1; units <= 48; units += 1)
     for (int items = 1; items <= 9; items += 4)
       for (int L = 0; L < units * items; ++L) {
@@ -191,6 +258,14 @@ def test_tile_bookkeeping_matches_brute_force():
     seen = {}
     for ln in lines:
         f = ln.split()
+        if f[0] == "S":
+            lo, hi, total, mx, off, ln = map(int, f[1:])
+            # the span is inside [0, total], no longer than mx, and equals
+            # [lo, hi) whenever that is a well-formed range of length <= mx
+            assert 0 <= off <= total and 0 <= ln <= mx and off + ln <= total
+            if 0 <= lo <= hi <= total and hi - lo <= mx:
+                assert (off, ln) == (lo, hi - lo)
+            continue
         if f[0] == "X":
             units, items, L, unit, item = map(int, f[1:])
             assert 0 <= unit < units and 0 <= item < items

@@ -37,6 +37,11 @@ def test_kernel_to_entry_point():
     assert bench._call_of("_ZN2fa21bwd_preprocess_kernelILi128ELb0ELb0EEEvPKDF16bPKvPfS5_x") == "fa_bwd"
     assert bench._call_of("_ZN2fa21bwd_preprocess_kernelILi128ELb0ELb1EEEvPKDF16bPKvPfS5_x") == "fa_bwd_atomic"
     assert bench._call_of("__amd_rocclr_copyBuffer") is None
+    assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, true>(fa::FwdArgs)") == "fa_fwd_varlen"
+    assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false>(fa::FwdArgs)") == "fa_fwd"
+    assert bench._call_of("void fa::bwd_dkdv_kernel<128, true, false, true>(fa::BwdArgs)") == "fa_bwd_varlen"
+    assert bench._call_of("void fa::bwd_dq_kernel<128, true, true>(fa::BwdArgs)") == "fa_bwd_varlen"
+    assert bench._call_of("void fa::bwd_dq_kernel<128, true, false>(fa::BwdArgs)") == "fa_bwd"
 
 
 def test_summarize_profiles_calibrates_and_records(tmp_path, capsys):
