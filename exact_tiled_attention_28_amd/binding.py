@@ -59,10 +59,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for fn in (lib.fa_bwd, lib.fa_bwd_atomic):
         fn.restype = _c_int
         fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
-    lib.fa_fwd_varlen.restype = _c_int
-    lib.fa_fwd_varlen.argtypes = [_c_ptr] * 7 + [_c_int] * 8 + [_c_float] + [_c_int] * 3 + [_c_ptr]
-    lib.fa_bwd_varlen.restype = _c_int
-    lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    # (looked up only if present, so that an older build still loads for the
+    # fixed-length calls; calling a missing function raises AttributeError)
+    if hasattr(lib, "fa_fwd_varlen"):
+        lib.fa_fwd_varlen.restype = _c_int
+        lib.fa_fwd_varlen.argtypes = [_c_ptr] * 7 + [_c_int] * 8 + [_c_float] + [_c_int] * 3 + [_c_ptr]
+    if hasattr(lib, "fa_bwd_varlen"):
+        lib.fa_bwd_varlen.restype = _c_int
+        lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p

@@ -908,7 +908,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // skips tiles entirely above a wavefront's rows and masks tiles that cross
   // the diagonal or the end of K/V; as in the forward, every tile before the
   // last BR / BC ones is unmasked for every wavefront (Q tiles start at
-  // multiples of BR), so the main loop runs the unmasked body only.
+  // multiples of BR), so the non-causal main loop runs the unmasked body only.
   auto step = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Kn, char* Vn)
                   __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
@@ -930,22 +930,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
   };
 
-  constexpr int NTAIL = BR / BC;
-  const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
   // A sequence with no keys (variable-length batches only) has dQ = 0.
   if (n_kv > 0) issue_tile(0, sK0, sV0);
   wait_vmem();
   __syncthreads();
   int jt = 0;
-  for (; jt + 1 < n_main; jt += 2) {
-    step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
-    step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
-  }
-  for (; jt < n_kv; ++jt) {
-    if (jt & 1)
-      step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
-    else
+  if constexpr (CAUSAL) {
+    // Causal: every step takes the generic form (measured: splitting off the
+    // unmasked steps costs more registers than it saves here).
+    for (; jt + 1 < n_kv; jt += 2) {
       step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+      step(std::true_type{}, jt + 1, sK1, sV1, sK0, sV0);
+    }
+    if (jt < n_kv) step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+  } else {
+    constexpr int NTAIL = BR / BC;
+    const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
+    for (; jt + 1 < n_main; jt += 2) {
+      step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
+      step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
+    }
+    for (; jt < n_kv; ++jt) {
+      if (jt & 1)
+        step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
+      else
+        step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+    }
   }
 
   if (qrow < Nq) {
