@@ -142,3 +142,10 @@ def make_varlen_inputs(seed: int, lengths_q, lengths_k, n_q_heads: int, n_kv_hea
     if do is not None:
         do = round_to_bf16(do)[0]
     return VarlenInputs(q, k, v, do, cu_q, cu_k, int(lq.max(initial=0)), int(lk.max(initial=0)))
+
+
+def make_signs(seed: int, head_dim: int) -> np.ndarray:
+    """Random +1/-1 per channel (int8 [head_dim]) for the random-sign Hadamard
+    transform of the FP8 path, drawn once and passed to both sides."""
+    rng = np.random.default_rng(seed)
+    return np.where(rng.random(head_dim) < 0.5, -1, 1).astype(np.int8)

@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     probabilities_head,
     row_dot,
 )
+from . import fp8  # noqa: F401,E402
