@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
     p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
+    p.add_argument("--fp8", action="store_true",
+                   help="time fa_quantize_fp8 (Q and K) + fa_fwd_fp8 beside fa_fwd (default workload, or --workload)")
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
                    help="summarise rocprofv3 output under DIR/{trace,fetch,write} (no GPU needed) and record "
                         "the HBM bytes per launch for the current kernel sources")
@@ -200,6 +202,61 @@ def bench_varlen(args):
     print(json.dumps(out), flush=True)
 
 
+MI355X_FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA
+
+
+def bench_fp8(args):
+    """Time the FP8 forward path on one forward workload: fa_quantize_fp8 of
+    Q and of K (random-sign Hadamard transform, seed = the workload's) and
+    fa_fwd_fp8 (bf16 O), with fa_fwd on the same inputs beside it. Prints one
+    JSON line. The roofline of fa_fwd_fp8 counts S = Q K^T at the fp8 peak
+    and O = P V at the bf16 peak: half of the flops each."""
+    import torch
+    from exact_tiled_attention_28_amd.inputs import make_signs
+    w = WORKLOADS[args.workload or STEP_WORKLOAD]
+    if w.passes != "fwd" or w.head_dim != 128 or w.dtype != "bf16":
+        raise SystemExit(f"--fp8 needs a bf16 forward workload with head_dim 128, not {w.name}")
+    _, q, k, v, _ = device_inputs(w, with_do=False)
+    step = Step(w, q, k, v, q)
+    signs = torch.from_numpy(make_signs(w.seed, w.head_dim)).cuda()
+    qc, qs = binding.quantize_fp8(q, signs)
+    kc, ks = binding.quantize_fp8(k, signs)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def quant_q():
+        binding.quantize_fp8(q, signs, qc, qs, stream=stream)
+
+    def quant_k():
+        binding.quantize_fp8(k, signs, kc, ks, stream=stream)
+
+    def fwd8():
+        binding.forward_fp8(qc, qs, kc, ks, v, w.scale, w.causal, o=o, lse=lse, stream=stream)
+
+    _, per_call, _ = time_calls(None, [quant_q, quant_k, fwd8, step.fwd], args.steps, args.warmup)
+    med = [float(np.median(per_call[:, i])) for i in range(4)]
+    avg8 = float(np.mean(per_call[:, 2]))
+    ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    peak_mixed = 2.0 / (1.0 / MI355X_FP8_PEAK_TFLOPS + 1.0 / MI355X_BF16_PEAK_TFLOPS)
+    tf8 = ff / (med[2] * 1e-3) / 1e12
+    ach = ff / (avg8 * 1e-3) / 1e12
+    el = w.batch * w.n_q_heads * w.seqlen * w.head_dim
+    qbytes = el * 2 + el + w.batch * w.n_q_heads * (-(-w.seqlen // 64)) * 4  # bf16 in, codes + scales out
+    out = {"workload": f"{w.name}: fa_quantize_fp8(Q), fa_quantize_fp8(K), fa_fwd_fp8 (bf16 O)",
+           "quantize_q_ms": round(med[0], 4), "quantize_q_gbps": round(qbytes / (med[0] * 1e-3) / 1e9, 1),
+           "quantize_k_ms": round(med[1], 4),
+           "fwd_fp8_ms": round(med[2], 4), "fwd_fp8_tflops": round(tf8, 2),
+           "fp8_path_ms": round(sum(med[:3]), 4),
+           "fp8_path_tflops": round(ff / (sum(med[:3]) * 1e-3) / 1e12, 2),
+           "fwd_bf16_ms": round(med[3], 4), "fwd_bf16_tflops": round(ff / (med[3] * 1e-3) / 1e12, 2),
+           "roofline": {"kernel": "fa_fwd_fp8 (fwd_fp8_kernel)", "bound": "mfma", "achieved": round(ach, 2),
+                        "peak": round(peak_mixed, 1), "unit": "TFLOP/s", "frac": round(ach / peak_mixed, 4),
+                        "peak_note": "half the flops (Q K^T) at the 5.0 PFLOP/s fp8 peak, half (P V) at the "
+                                     "2.5166 PFLOP/s bf16 peak", "avg_launch_ms": round(avg8, 4)}}
+    print(json.dumps(out), flush=True)
+
+
 def csrc_sha256():
     """sha256 over the kernel sources (file names and contents, sorted)."""
     import hashlib
@@ -219,6 +276,8 @@ CALL_KERNELS = {
     "fa_fwd": ("void fa::fwd_kernel<", "void fa::fwd_pp_kernel<"),
     "fa_bwd": ("void fa::bwd_dkdv_kernel<", "void fa::bwd_dq_kernel<"),
     "fa_bwd_atomic": ("void fa::bwd_kernel<",),
+    "fa_quantize_fp8": ("void fa::quantize_fp8_kernel<",),
+    "fa_fwd_fp8": ("void fa::fwd_fp8_kernel<",),
 }
 
 
@@ -382,6 +441,8 @@ def main():
         sys.exit(2)
     binding.load_library()
 
+    if args.fp8:
+        return bench_fp8(args)
     if args.workload:
         return bench_one(args)
     if args.varlen:

@@ -19,12 +19,17 @@ from .binding import (  # noqa: F401
     fa_bwd_atomic,
     fa_bwd_varlen,
     fa_bwd_workspace_bytes,
+    fa_fp8_scales_count,
     fa_fwd,
+    fa_fwd_fp8,
     fa_fwd_varlen,
     fa_last_error,
+    fa_quantize_fp8,
     fa_status_string,
     fa_version,
     forward,
+    forward_fp8,
     forward_varlen,
     load_library,
+    quantize_fp8,
 )

@@ -67,6 +67,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if hasattr(lib, "fa_bwd_varlen"):
         lib.fa_bwd_varlen.restype = _c_int
         lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    if hasattr(lib, "fa_quantize_fp8"):
+        lib.fa_quantize_fp8.restype = _c_int
+        lib.fa_quantize_fp8.argtypes = [_c_ptr] * 4 + [_c_int] * 5 + [_c_ptr]
+        lib.fa_fp8_scales_count.restype = ctypes.c_size_t
+        lib.fa_fp8_scales_count.argtypes = [_c_int] * 3
+        lib.fa_fwd_fp8.restype = _c_int
+        lib.fa_fwd_fp8.argtypes = [_c_ptr] * 7 + [_c_int] * 6 + [_c_float] + [_c_int] * 2 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -116,6 +123,21 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batc
     return load_library().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch,
                                         max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim,
                                         scale, causal, in_dtype, o_dtype, grad_dtype, stream)
+
+
+def fa_quantize_fp8(x, codes, block_scales, signs, batch, n_heads, seqlen, head_dim, in_dtype, stream) -> int:
+    return load_library().fa_quantize_fp8(x, codes, block_scales, signs, batch, n_heads, seqlen, head_dim, in_dtype,
+                                          stream)
+
+
+def fa_fp8_scales_count(batch, n_heads, seqlen) -> int:
+    return load_library().fa_fp8_scales_count(batch, n_heads, seqlen)
+
+
+def fa_fwd_fp8(q_codes, q_scales, k_codes, k_scales, v, o, lse, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+               head_dim, scale, causal, out_dtype, stream) -> int:
+    return load_library().fa_fwd_fp8(q_codes, q_scales, k_codes, k_scales, v, o, lse, batch, n_q_heads, n_kv_heads,
+                                     seqlen_q, seqlen_k, head_dim, scale, causal, out_dtype, stream)
 
 
 def fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q) -> int:
@@ -252,3 +274,49 @@ def backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_seqlen_q, max_seqlen_k,
                        float(scale), int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
     _check(rc, "fa_bwd_varlen")
     return dq, dk, dv, ws[:Hq * total_q].view(Hq, total_q)
+
+
+def quantize_fp8(x, signs=None, codes=None, scales=None, stream=None):
+    """FP8 codes (uint8 [B,H,N,d]) and power-of-two block scales (fp32
+    [B,H,ceil(N/64)]) of x [B,H,N,d] (contiguous bf16 on the GPU); signs is an
+    int8 [d] tensor of +1/-1 (random-sign Hadamard transform) or None."""
+    import torch
+    B, H, N, d = x.shape
+    if codes is None:
+        codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, -(-N // 64)), dtype=torch.float32, device=x.device)
+    for t in (x, codes, scales) + ((signs,) if signs is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if signs is not None and (signs.dtype != torch.int8 or signs.numel() != d):
+        raise TypeError("signs must be an int8 tensor of head_dim entries")
+    rc = fa_quantize_fp8(x.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                         signs.data_ptr() if signs is not None else None, B, H, N, d, _dtype_code(x),
+                         _stream_handle(stream))
+    _check(rc, "fa_quantize_fp8")
+    return codes, scales
+
+
+def forward_fp8(q_codes, q_scales, k_codes, k_scales, v, scale, causal, out_dtype=None, o=None, lse=None,
+                stream=None):
+    """O, L of the FP8 forward from codes and block scales written by
+    quantize_fp8 (same signs for Q and K); v [B,Hkv,Nk,128] bf16."""
+    import torch
+    B, Hq, Nq, d = q_codes.shape
+    Hkv, Nk = k_codes.shape[1], k_codes.shape[2]
+    oc = FA_DTYPE_BF16 if out_dtype in (None, torch.bfloat16) else FA_DTYPE_F32
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=_torch_dtype(oc), device=q_codes.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q_codes.device)
+    for t in (q_codes, q_scales, k_codes, k_scales, v, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    rc = fa_fwd_fp8(q_codes.data_ptr(), q_scales.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(), v.data_ptr(),
+                    o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), oc,
+                    _stream_handle(stream))
+    _check(rc, "fa_fwd_fp8")
+    return o, lse

@@ -21,7 +21,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libfa.so")
 ROOT = os.path.dirname(PKG)
 
-HIP_SOURCES = ["fa_fwd.hip", "fa_bwd.hip"]
+HIP_SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip"]
 HOST_SOURCES = ["fa_api.cpp"]
 ARCH = "gfx950"
 

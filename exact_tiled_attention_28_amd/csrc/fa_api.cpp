@@ -1,6 +1,7 @@
 // fa_api.cpp — the C ABI declared in include/fa.h: validate on the host,
 // pick the kernel instantiation, launch on the caller's stream, return.
 #include <cmath>
+#include <cstdint>
 #include <string>
 
 #include "../../include/fa.h"
@@ -184,6 +185,66 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   hipError_t e = fa::launch_bwd_varlen(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
                                        (hipStream_t)stream);
   return hip_status(e, "fa_bwd_varlen launch");
+}
+
+int fa_quantize_fp8(const void* x, void* codes, float* block_scales, const signed char* signs, int batch,
+                    int n_heads, int seqlen, int head_dim, int in_dtype, void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_ptr(x, "x", err)) || (rc = fa::check_ptr(codes, "codes", err))) return fail(rc, err);
+  if (block_scales == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "block_scales is NULL");
+  if (reinterpret_cast<uintptr_t>(block_scales) & 3u)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_scales is not 4-byte aligned");
+  if (batch < 1 || n_heads < 1 || seqlen < 1) return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (!fa::valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARGUMENT, "in_dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16");
+  if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "fa_quantize_fp8 takes bf16 input");
+  if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
+                                                     " unsupported (64 or 128)");
+  if ((long long)seqlen * head_dim >= (1LL << 31)) return fail(FA_ERR_INVALID_ARGUMENT, "seqlen * head_dim must be below 2^31");
+  if ((long long)batch * n_heads * ((seqlen + 63) / 64) >= (1LL << 31))
+    return fail(FA_ERR_INVALID_ARGUMENT, "batch * n_heads * blocks too large");
+  hipError_t e = fa::launch_quantize_fp8(x, codes, block_scales, signs, batch * n_heads, seqlen, head_dim,
+                                         (hipStream_t)stream);
+  return hip_status(e, "fa_quantize_fp8 launch");
+}
+
+int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes, const float* k_scales, const void* v,
+               void* o, float* lse, int batch, int n_q_heads, int n_kv_heads, int seqlen_q, int seqlen_k,
+               int head_dim, float scale, int causal, int out_dtype, void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_fwd(q_codes, k_codes, v, o, lse,
+                          fa::Shape{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim}, scale, causal,
+                          FA_DTYPE_BF16, out_dtype, err)))
+    return fail(rc, err);
+  if (q_scales == nullptr || k_scales == nullptr)
+    return fail(FA_ERR_INVALID_ARGUMENT, q_scales == nullptr ? "q_scales is NULL" : "k_scales is NULL");
+  if ((reinterpret_cast<uintptr_t>(q_scales) & 3u) || (reinterpret_cast<uintptr_t>(k_scales) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "q_scales / k_scales must be 4-byte aligned");
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward supports head_dim 128");
+  fa::FwdArgs a{};
+  a.q = q_codes;
+  a.k = k_codes;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  a.q_scales = q_scales;
+  a.k_scales = k_scales;
+  hipError_t e = fa::launch_fwd_fp8(a, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  return hip_status(e, "fa_fwd_fp8 launch");
+}
+
+size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen) {
+  if (batch <= 0 || n_heads <= 0 || seqlen <= 0) return 0;
+  return (size_t)batch * (size_t)n_heads * (size_t)((seqlen + 63) / 64);
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q) {

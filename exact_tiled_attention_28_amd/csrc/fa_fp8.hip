@@ -1,0 +1,426 @@
+// fa_fp8.hip — FP8 (OCP e4m3) forward with incoherent processing for gfx950.
+//
+// The FlashAttention-3 news page ("Độ chính xác thấp FP8 và incoherent
+// processing") quantizes Q and K to FP8 after multiplying both by the same
+// random orthogonal matrix, a Hadamard transform with random signs: since
+// (Q M)(K M)^T = Q K^T for orthogonal M, the scores are unchanged while
+// large-magnitude outlier channels are spread over all channels, which
+// lowers the quantization error; the transform costs O(d log d) per row.
+//
+// Two entry points:
+//   * fa_quantize_fp8: y = FWHT(x o s) / sqrt(d) per row (s = +-1 signs; no
+//     transform if none are given), then per 64-row block a power-of-two
+//     scale 2^e, the smallest with max|y| <= 448 * 2^e, and e4m3 codes of
+//     y / 2^e rounded to nearest, ties to even. Every step is exact or a
+//     fixed sequence of fp32 operations (the butterflies a+b, a-b in stage
+//     order h = 1, 2, ..., d/2, then one multiply by fp32(1/sqrt d)), so the
+//     codes are reproducible bit for bit.
+//   * fa_fwd_fp8: the forward of fa_fwd with S^T = K Q^T computed from the
+//     codes by v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 accumulate) and
+//     scaled by the two block scales in fp32 before the softmax; P V stays in
+//     bf16 as in fa_fwd.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// ---------------------------------------------------------------------------
+// e4m3 (OCP FP8 E4M3FN: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// largest finite 448, subnormal step 2^-9) code of |v| <= 448, round to
+// nearest, ties to even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned e4m3_code(float v) {
+  const unsigned sign = __float_as_uint(v) >> 31;
+  const float a = fabsf(v);
+  unsigned mag;
+  if (a >= 0.015625f) {  // 2^-6: normal range
+    // Keep 3 of the 23 fp32 mantissa bits, rounding the dropped 20 bits to
+    // nearest even; a carry out of the mantissa bumps the exponent, which is
+    // what the encoding needs.
+    const unsigned u = __float_as_uint(a);
+    const unsigned r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // (biased fp32 exponent << 3) | m3
+    mag = r - ((127u - 7u) << 3);
+  } else {
+    // Subnormal: a / 2^-9 rounded to nearest even integer (0..8; 8 is the
+    // smallest normal, code 0x08).
+    mag = (unsigned)__builtin_rintf(a * 512.0f);
+  }
+  return (sign << 7) | mag;
+}
+
+// Exponent e of the smallest power of two with amax <= 448 * 2^e (amax > 0,
+// finite): with amax = m 2^E, m in [1, 2), and 448 = 1.75 2^8,
+// e = E - 8 + (m > 1.75). Clamped to keep 2^e a normal fp32 number.
+__device__ __forceinline__ int block_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const unsigned u = __float_as_uint(amax);
+  const int E = (int)((u >> 23) & 0xFFu) - 127;
+  const unsigned mant = u & 0x7FFFFFu;
+  const int e = E - 8 + (mant > 0x600000u ? 1 : 0);  // m > 1.75 <=> mantissa bits > 0.75 * 2^23
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+// ---------------------------------------------------------------------------
+// Quantize pass: one workgroup (4 wavefronts) per 64-row block of one head.
+// A row is spread over D/8 lanes holding 8 consecutive elements each, so the
+// butterflies of stages h < 8 stay inside a lane and stages h >= 8 exchange
+// with lane ^ (h / 8).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) quantize_fp8_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales, const signed char* signs,
+                                                            int N, int n_blocks) {
+  constexpr int LPR = D / 8;         // lanes per row
+  constexpr int RPP = 64 / LPR;      // rows per wavefront pass
+  constexpr int PASSES = 16 / RPP;   // each wavefront handles 16 rows of the block
+  __shared__ float wmax[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int head = blockIdx.x / n_blocks, blk = blockIdx.x % n_blocks;
+  const int c0 = (lane % LPR) * 8;   // first element of this lane
+  const size_t head_off = (size_t)head * N * D;
+
+  float sg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sg[e] = signs ? (float)signs[c0 + e] : 1.0f;
+  const float inv_sqrt_d = D == 64 ? 0.125f : 0.08838834764831845f;
+
+  float y[PASSES][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = blk * 64 + w * 16 + p * RPP + lane / LPR;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (row < N) {
+      const u32x4 raw = *(const u32x4*)(x + head_off + (size_t)row * D + c0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(raw[i] << 16);
+        v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+      }
+    }
+    if (signs) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= sg[e];
+      // stages h = 1, 2, 4 inside the lane
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!(e & h)) {
+            const float a = v[e], b = v[e + h];
+            v[e] = a + b;
+            v[e + h] = a - b;
+          }
+      // stages h = 8 .. D/2 across lanes: the partner holds element c +- h
+#pragma unroll
+      for (int h = 8; h < D; h <<= 1) {
+        const int m = h / 8;
+        const bool lower = ((lane % LPR) & m) == 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o = __shfl_xor(v[e], m, 64);
+          v[e] = lower ? v[e] + o : o - v[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= inv_sqrt_d;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[p][e] = v[e];
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+  }
+  // block max over the 4 wavefronts
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (lane == 0) wmax[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e = block_scale_exp(amax);
+  if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, e);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = blk * 64 + w * 16 + p * RPP + lane / LPR;
+    if (row < N) {
+      unsigned lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_code(ldexpf(y[p][i], -e)) << (8 * i);
+        hi |= e4m3_code(ldexpf(y[p][i + 4], -e)) << (8 * i);
+      }
+      *(u32x2*)(codes + head_off + (size_t)row * D + c0) = u32x2{lo, hi};
+    }
+  }
+}
+
+hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
+                               int N, int head_dim, hipStream_t s) {
+  const int n_blocks = ceil_div(N, 64);
+  const long long grid = (long long)heads * n_blocks;
+  if (head_dim == 64)
+    hipLaunchKernelGGL((quantize_fp8_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, (const __bf16*)x,
+                       (uint8_t*)codes, scales, signs, N, n_blocks);
+  else
+    hipLaunchKernelGGL((quantize_fp8_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, (const __bf16*)x,
+                       (uint8_t*)codes, scales, signs, N, n_blocks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// FP8 forward, d = 128: fwd_kernel's tiling (4 wavefronts x 32 query rows,
+// 64-key tiles, K/V double-buffered in LDS by HBM -> LDS loads) with the K
+// tile held as e4m3 codes (8 KiB, rows of 128 bytes) and S^T = K Q^T formed
+// by two 32x32x64 FP8 MFMAs per 32-key block. For those MFMAs a lane of
+// half-wave g supplies, in both operands, the 32 codes of head-dim range
+// [64 ks + 32 g, +32) of its key (A) or query (B) row: A and B then put the
+// same channel in the same slot, and the output has the 32x32 layout of the
+// bf16 MFMA. The 64-row scale blocks line up with the Q rows of a wavefront
+// (32 rows inside one block) and with a K tile (64 rows = one block), so the
+// scores of a tile are scaled by one scalar s_q s_k, folded into the base-2
+// softmax constant.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL, bool OUTF32>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_fp8_kernel(FwdArgs a) {
+  constexpr int D = 128, NW = 4, BR = 128, BC = 64, NKB = 2, NKS = D / 64, NDB = D / 32;
+  constexpr int KROWB = D, KRC = KROWB / 16, KTILEB = BC * KROWB, KCPW = KTILEB / (1024 * NW);  // fp8 K tile
+  constexpr int VROWB = D * 2, VRC = VROWB / 16, VTILEB = BC * VROWB, VCPW = VTILEB / (1024 * NW);  // bf16 V
+  static_assert(KTILEB % (1024 * NW) == 0 && VTILEB % (1024 * NW) == 0, "tiles must split into whole wave loads");
+
+  __shared__ __attribute__((aligned(16))) char sK0[KTILEB];
+  __shared__ __attribute__((aligned(16))) char sV0[VTILEB];
+  __shared__ __attribute__((aligned(16))) char sK1[KTILEB];
+  __shared__ __attribute__((aligned(16))) char sV1[VTILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+
+  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
+  const int b = ui.unit / a.Hkv;
+  const int hkv = ui.unit % a.Hkv;
+  const int rank = ui.item / a.G;
+  const int hq = hkv * a.G + ui.item % a.G;
+  const int qt = CAUSAL ? (a.n_q_tiles - 1 - rank) : rank;
+  const int q0 = qt * BR;
+  const int q0w = q0 + 32 * w;
+  const int qrow = q0w + l32;
+  const int Nq = a.Nq, Nk = a.Nk;
+
+  const size_t qhead = (size_t)(b * a.Hq + hq) * Nq;
+  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * Nk;
+  const char* __restrict__ Kh = (const char*)a.k + kvhead * KROWB;
+  const char* __restrict__ Vh = (const char*)a.v + kvhead * VROWB;
+  const int nqb = ceil_div(Nq, 64), nkb = ceil_div(Nk, 64);
+  // A wavefront whose rows all lie past the end (last query tile) stores
+  // nothing; its block index is clamped to stay inside the scale array.
+  const float sq = a.q_scales[(size_t)(b * a.Hq + hq) * nqb + min(q0w >> 6, nqb - 1)];
+  const float* __restrict__ sk = a.k_scales + (size_t)(b * a.Hkv + hkv) * nkb;
+
+  // Q codes (B operand): 32 bytes of head-dim range [64 ks + 32 g, +32). A
+  // negative scale flips the sign bit of every code (exact).
+  i32x8 qf[NKS];
+  {
+    const char* Qr = (const char*)a.q + (qhead + qrow) * D;
+    const unsigned sign = a.neg ? 0x80808080u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+      if (qrow < Nq) {
+        x0 = *(const u32x4*)(Qr + 64 * ks + 32 * g);
+        x1 = *(const u32x4*)(Qr + 64 * ks + 32 * g + 16);
+      }
+      x0 ^= sign;
+      x1 ^= sign;
+      qf[ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  }
+
+  const int kv_end = kv_end_for(q0, BR, Nk, CAUSAL);
+  const int n_kv = ceil_div(kv_end, BC);
+
+  // HBM -> LDS staging of one K tile (codes) and one V tile (bf16); rows
+  // past the end repeat the last row (their scores are masked).
+  auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+#pragma unroll
+    for (int u = 0; u < KCPW; ++u) {
+      const int cb = (wu * KCPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / KRC, pc = idx % KRC;
+      const int lc = pc ^ swz<KRC>(row);
+      const int grow = min(kv0 + row, Nk - 1);
+      load_lds_16(Kh + (size_t)grow * KROWB + lc * 16, Kt + cb * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < VCPW; ++u) {
+      const int cb = (wu * VCPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / VRC, pc = idx % VRC;
+      const int lc = pc ^ swz<VRC>(row);
+      const int grow = min(kv0 + row, Nk - 1);
+      load_lds_16(Vh + (size_t)grow * VROWB + lc * 16, Vt + cb * 16);
+    }
+  };
+
+  int koff[NKS][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) koff[ks][h] = tile_off<KRC>(l32, (4 * ks + 2 * g + h) * 16);
+  int voff[NDB][2];
+  {
+    const int j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        voff[db][h] = tile_off<VRC>(4 * g + 8 * h + (j >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY;
+  float lsum = 0.0f;
+
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kv0 = jt * BC;
+    const float c = a.c * sq * sk[jt];  // |scale| log2(e) times the two block scales
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 k0 = *(const u32x4*)(Kt + koff[ks][0] + kb * 32 * KROWB);
+        const u32x4 k1 = *(const u32x4*)(Kt + koff[ks][1] + kb * 32 * KROWB);
+        const i32x8 ka = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3], (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf[ks], sacc[kb], 0, 0, 0, 0, 0, 0);
+      }
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < Nk && (!CAUSAL || key <= qrow);
+          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    const float mxs = half_swap_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mxs > m) != 0) {
+      const float m_new = fmaxf(m, mxs);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
+        if constexpr (MASK) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
+        sacc[kb][r] = p;
+        rs += p;
+      }
+    lsum += rs;
+#pragma unroll
+    for (int t = 0; t < BC / 16; ++t) {
+      float pv[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) pv[v] = sacc[t >> 1][8 * (t & 1) + v];
+      const bf16x8 pb = to_bf16x8(pv);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vp = Vt + 16 * t * VROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][1]));
+        oacc[db] = mfma_bf16(cat4(lo, hi), pb, oacc[db]);
+      }
+    }
+  };
+
+  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) __attribute__((always_inline)) {
+    const int kv0 = jt * BC;
+    if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
+    const bool active = !CAUSAL || kv0 <= q0w + 31;
+    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > Nk);
+    if (active) {
+      if (need_mask)
+        body(std::true_type{}, jt, Kt, Vt);
+      else
+        body(std::false_type{}, jt, Kt, Vt);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  issue_tile(0, sK0, sV0);
+  wait_vmem();
+  __syncthreads();
+  int jt = 0;
+  for (; jt + 1 < n_kv; jt += 2) {
+    step(jt, sK0, sV0, sK1, sV1);
+    step(jt + 1, sK1, sV1, sK0, sV0);
+  }
+  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
+
+  const float lt = half_swap_add(lsum);
+  const float inv = 1.0f / lt;
+  if (qrow < Nq) {
+    const size_t orow = (qhead + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = db * 32 + 8 * a4 + 4 * g;
+        f32x4 ov = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                    oacc[db][4 * a4 + 3] * inv};
+        if constexpr (OUTF32)
+          *(f32x4*)((float*)a.o + orow + d0) = ov;
+        else
+          *(bf16x4*)((__bf16*)a.o + orow + d0) = __builtin_convertvector(ov, bf16x4);
+      }
+    if (g == 0) a.lse[qhead + qrow] = (m + fast_log2(lt)) * kLn2;
+  }
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a0, bool causal, bool out_f32, hipStream_t s) {
+  FwdArgs a = a0;
+  a.n_q_tiles = ceil_div(a.Nq, 128);
+  const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
+  if (causal) {
+    if (out_f32)
+      hipLaunchKernelGGL((fwd_fp8_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else {
+    if (out_f32)
+      hipLaunchKernelGGL((fwd_fp8_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -182,6 +182,55 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   int n_kv_heads, int head_dim, float scale, int causal,
                   int in_dtype, int o_dtype, int grad_dtype, void* stream);
 
+/*
+ * fa_quantize_fp8 — the FP8 quantization with incoherent processing of the
+ * FlashAttention-3 news page ("Độ chính xác thấp FP8 và incoherent
+ * processing"): each row x of a [B][H][N][d] bf16 tensor becomes
+ *   y = FWHT(x o s) / sqrt(d)       (s = signs, +-1 per channel; FWHT the
+ *                                    unnormalised Walsh-Hadamard transform)
+ * or y = x when signs is NULL; then every block of 64 rows (the last one may
+ * be shorter) of one (batch, head) gets the scale 2^e, the smallest power of
+ * two with max|y| <= 448 * 2^e and e >= -126 (e = 0 for an all-zero block;
+ * inputs must be finite), and its elements are stored as OCP FP8 E4M3
+ * codes of y / 2^e, rounded to nearest, ties to even. Applying the same
+ * signs to Q and K leaves Q K^T unchanged (the transform is orthogonal) while
+ * spreading outlier channels over all channels.
+ *   x            device, bf16 [B][H][N][d] (in_dtype must be FA_DTYPE_BF16),
+ *                16-byte aligned
+ *   codes        device, uint8 [B][H][N][d], 16-byte aligned, overwritten
+ *   block_scales device, fp32 [B][H][ceil(N/64)] (fa_fp8_scales_count
+ *                entries), overwritten with the powers of two 2^e
+ *   signs        device int8 [d] of +1 / -1, or NULL for no transform
+ *   head_dim     64 or 128
+ * The transform runs in fp32 as a fixed sequence of butterflies (a + b,
+ * a - b) over stages h = 1, 2, 4, ..., d/2, then one multiply by
+ * fp32(1/sqrt d), so the codes are reproducible bit for bit.
+ */
+int fa_quantize_fp8(const void* x, void* codes, float* block_scales,
+                    const signed char* signs, int batch, int n_heads,
+                    int seqlen, int head_dim, int in_dtype, void* stream);
+
+/* Number of block scales fa_quantize_fp8 writes: batch * n_heads *
+ * ceil(seqlen / 64) (0 for non-positive arguments). */
+size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen);
+
+/*
+ * fa_fwd_fp8 — fa_fwd with the scores formed in FP8: q_codes / k_codes and
+ * q_scales / k_scales as written by fa_quantize_fp8 (with the same signs for
+ * Q and K), S = scale * (Q_codes 2^e_q)(K_codes 2^e_k)^T by FP8 matrix cores
+ * (fp32 accumulate, one block scale pair per 64 x 64 score tile), then the
+ * online softmax and O = P V exactly as fa_fwd (P rounded to bf16, V bf16).
+ *   q_codes [B][Hq][Nq][128], k_codes [B][Hkv][Nk][128] uint8, 16-byte aligned
+ *   q_scales [B][Hq][ceil(Nq/64)], k_scales [B][Hkv][ceil(Nk/64)] fp32
+ *   v [B][Hkv][Nk][128] bf16; o, lse, scale, causal, out_dtype as in fa_fwd.
+ * head_dim must be 128 (else FA_ERR_UNSUPPORTED).
+ */
+int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes,
+               const float* k_scales, const void* v, void* o, float* lse,
+               int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
+               int seqlen_k, int head_dim, float scale, int causal,
+               int out_dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd and fa_bwd_atomic need: 4 * batch * n_q_heads * seqlen_q
  * (the fp32 vector D, page 6.2 section 7.3). Returns 0 for non-positive
  * arguments. */

@@ -1,0 +1,258 @@
+"""The FP8 path on the GPU (fa_quantize_fp8 and fa_fwd_fp8 through the C ABI)
+against the oracle's FP8 definition (oracle/fp8.py) on the same seeded bf16
+inputs and the same random signs.
+
+* Codes and block scales must be bit-exact: the oracle takes every rounding
+  decision in the kernel's precision (float32 butterflies, then e4m3 round
+  to nearest even of an exact power-of-two quotient).
+* O and L of fa_fwd_fp8 must match the oracle's FP8 forward (the plain fp64
+  attention of the dequantized Q, K and the bf16 V) within the bounds of the
+  bf16 forward, O max-abs 1e-2 and L 1e-3, plus a bound for the one step
+  whose precision the hardware fixes: the FP8 matrix instruction sums its 64
+  exact products in a fixed-point window anchored at the largest one
+  (measured on gfx950: terms 2^-13 below the leading bit of the largest
+  product are kept, 2^-14 are dropped), then adds the sum to the fp32
+  accumulator. Each of the 64 terms of one instruction is then off by less
+  than 2^(E - 12), E = floor(log2 max|product|) (one bit of margin for where
+  the window is anchored), so a score is off by at most
+  delta_ij = |scale| sq_i sk_j sum over the two 64-channel halves 64 * 2^(E - 12),
+  L_i by at most max_j delta_ij and O_i by (exp(2 max_j delta_ij) - 1) max|v|
+  (the softmax weights move by at most that factor). On inputs without
+  outlier channels the bf16 bounds alone are asserted too.
+* On inputs with outlier entries, the transform with random signs lowers
+  the error against exact attention (the property the method is for).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8 as ofp8
+from exact_tiled_attention_28_amd import binding
+from exact_tiled_attention_28_amd.inputs import make_signs, round_to_bf16
+from exact_tiled_attention_28_amd.workloads import WORKLOADS
+from tests.gpu_util import announce, bf16_half_ulp, gen, host, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_dev(x):
+    import torch
+    _, bits = round_to_bf16(np.ascontiguousarray(x, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def _signs_dev(signs):
+    import torch
+    return None if signs is None else torch.from_numpy(signs.copy()).cuda()
+
+
+def window_bound(qc, qs, kc, ks, scale, causal, rows=None):
+    """max_j delta_ij (see the module doc) for the query rows `rows` (all by
+    default) of one head, over the keys each row sees."""
+    qv, kv = ofp8.e4m3_decode(qc), ofp8.e4m3_decode(kc)
+    rows = np.arange(qv.shape[0]) if rows is None else np.asarray(rows)
+    sq = np.repeat(np.asarray(qs, dtype=np.float64), 64)[rows]
+    sk = np.repeat(np.asarray(ks, dtype=np.float64), 64)[:kv.shape[0]]
+    out = np.empty(rows.size)
+    for n, i in enumerate(rows):
+        keys = kv[:i + 1] if causal else kv
+        tot = np.zeros(keys.shape[0])
+        for c0 in range(0, qv.shape[1], 64):
+            p = np.abs(qv[i, c0:c0 + 64] * keys[:, c0:c0 + 64]).max(axis=1)
+            e = np.floor(np.log2(np.where(p > 0, p, 1.0)))
+            tot += np.where(p > 0, 64 * np.exp2(e - 12), 0.0)
+        out[n] = abs(scale) * sq[n] * np.max(tot * sk[:keys.shape[0]])
+    return out
+
+
+def _assert_within(O_got, L_got, O_ref, L_ref, v_absmax, bound, where):
+    """O and L of one head (rows x d, rows) within 1e-2 / 1e-3 plus the window
+    bound of each row."""
+    dl = np.abs(L_got - L_ref)
+    do = np.max(np.abs(O_got - O_ref), axis=-1)
+    assert np.all(dl <= 1e-3 + bound), f"L {where}: worst excess {np.max(dl - 1e-3 - bound):.3e}"
+    assert np.all(do <= 1e-2 + np.expm1(2 * bound) * v_absmax), f"O {where}"
+
+
+def _quantize_both(x_host, x_dev, signs):
+    codes, scales = binding.quantize_fp8(x_dev, _signs_dev(signs))
+    oc, osc = ofp8.quantize(x_host, signs)
+    return codes.cpu().numpy(), scales.cpu().numpy(), oc, osc
+
+
+QUANT_CASES = [
+    # (B, H, N, d, with signs, outlier channels)
+    (2, 3, 200, 128, True, 2),
+    (1, 2, 64, 64, True, 0),
+    (1, 1, 1, 128, False, 0),
+    (2, 2, 130, 64, False, 3),
+    (1, 4, 333, 128, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{'s' if c[4] else ''}"
+                                                   for c in QUANT_CASES])
+def test_quantize_fp8_bit_exact(case):
+    B, H, N, d, with_signs, outl = case
+    announce(f"fa_quantize_fp8 {case}")
+    inp = gen(21 + N, B, H, H, N, N, d, outliers=outl)
+    q, _, _, _ = upload(inp)
+    signs = make_signs(5 + d, d) if with_signs else None
+    codes, scales, oc, osc = _quantize_both(inp.q, q, signs)
+    np.testing.assert_array_equal(scales, osc.astype(np.float32))
+    np.testing.assert_array_equal(codes, oc)
+
+
+def test_quantize_fp8_ties_subnormals_and_extreme_blocks():
+    # No transform, so y = x: block 0 holds 448 (scale 1) with exact ties
+    # between e4m3 values and subnormal-range values; block 1 is all zeros
+    # (scale 1, codes 0); block 2 is tiny (the scale is clamped at 2^-126);
+    # block 3 is huge; block 4 holds a single negative zero row.
+    d, N = 64, 4 * 64 + 1
+    x = np.zeros((1, 1, N, d), dtype=np.float32)
+    ties = np.array([448, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -5 * 2.0 ** -10, 2.0 ** -6 + 2.0 ** -10,
+                     15 * 2.0 ** -4 + 2.0 ** -5, 240 + 8, 2.0 ** -11, 0.0], dtype=np.float32)
+    rng = np.random.default_rng(8)
+    x[0, 0, :64] = rng.choice(ties, size=(64, d))
+    x[0, 0, 0, 0] = 448.0
+    # normal fp32 values with max below 448 * 2^-126 = 1.75 * 2^-118
+    mag = rng.uniform(2.0 ** -119, 1.5 * 2.0 ** -118, (64, d)) * rng.choice([-1.0, 1.0], (64, d))
+    x[0, 0, 128:192] = mag.astype(np.float32)
+    x[0, 0, 192:256] = rng.standard_normal((64, d)).astype(np.float32) * np.float32(1e30)
+    x[0, 0, 256] = -0.0
+    x = round_to_bf16(x)[0]
+    announce("fa_quantize_fp8 ties/subnormals/extreme blocks")
+    codes, scales, oc, osc = _quantize_both(x, _bf16_dev(x), None)
+    assert osc[0, 0, 0] == 1.0 and osc[0, 0, 1] == 1.0 and osc[0, 0, 2] == 2.0 ** -126
+    np.testing.assert_array_equal(scales, osc.astype(np.float32))
+    np.testing.assert_array_equal(codes, oc)
+    assert np.all(codes[0, 0, 64:128] == 0) and np.all(codes[0, 0, 256] == 0x80)
+
+
+FWD_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, causal, with signs, outlier channels, scale)
+    (1, 4, 2, 300, 300, True, True, 4, None),
+    (2, 2, 2, 130, 257, False, False, 0, None),
+    (1, 2, 1, 1, 1, True, True, 0, None),
+    (1, 3, 1, 70, 600, False, True, 0, None),
+    (1, 2, 2, 200, 200, True, True, 2, -0.1),
+    (1, 2, 1, 64, 64, False, True, 0, 0.0),
+]
+
+
+def _fwd_id(c):
+    return f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}{'c' if c[5] else 'n'}{'s' if c[6] else ''}o{c[7]}" + \
+        ("" if c[8] is None else f"sc{c[8]}")
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[_fwd_id(c) for c in FWD_CASES])
+def test_fwd_fp8_parity(case):
+    import torch
+    B, Hq, Hkv, Nq, Nk, causal, with_signs, outl, scale = case
+    d = 128
+    scale = float(np.float32(1 / np.sqrt(d))) if scale is None else scale
+    announce(f"fa_fwd_fp8 {_fwd_id(case)}")
+    inp = gen(31 + Nq + Nk, B, Hq, Hkv, Nq, Nk, d, outliers=outl)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(7, d) if with_signs else None
+    qc, qs, oqc, oqs = _quantize_both(inp.q, q, signs)
+    kc, ks, okc, oks = _quantize_both(inp.k, k, signs)
+    np.testing.assert_array_equal(qc, oqc)
+    np.testing.assert_array_equal(kc, okc)
+    dq_c, dq_s = binding.quantize_fp8(q, _signs_dev(signs))
+    dk_c, dk_s = binding.quantize_fp8(k, _signs_dev(signs))
+    o32, lse = binding.forward_fp8(dq_c, dq_s, dk_c, dk_s, v, scale, causal, out_dtype=torch.float32)
+    o16, lse16 = binding.forward_fp8(dq_c, dq_s, dk_c, dk_s, v, scale, causal, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    O, L = ofp8.forward_fp8(inp.q, inp.k, inp.v, scale, causal, signs)
+    O32, L32, O16 = host(o32), host(lse), host(o16)
+    err_o = np.max(np.abs(O32 - O))
+    err_l = np.max(np.abs(L32 - L))
+    worst_bound = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            bound = window_bound(oqc[b, h], oqs[b, h], okc[b, g], oks[b, g], scale, causal)
+            worst_bound = max(worst_bound, float(bound.max()))
+            vmax = np.max(np.abs(inp.v[b, g]))
+            _assert_within(O32[b, h], L32[b, h], O[b, h], L[b, h], vmax, bound, f"head {(b, h)}")
+            assert np.all(np.abs(O16[b, h] - O[b, h]) <= 1e-2 + bf16_half_ulp(O[b, h])
+                          + np.expm1(2 * bound)[:, None] * vmax), f"bf16 O head {(b, h)}"
+    print(f"max|dO|={err_o:.3e} max|dL|={err_l:.3e} window bound on dS <= {worst_bound:.3e}")
+    if outl == 0:
+        assert err_o <= 1e-2
+        assert err_l <= 1e-3
+    assert np.array_equal(host(lse16), L32), "L must not depend on the output dtype"
+
+
+def _sample_rows(rng, n, count):
+    rows = set(rng.choice(n, size=min(n, count), replace=False).tolist())
+    rows |= {0, 1, 63, 64, n - 1}
+    return np.array(sorted(rows))
+
+
+def test_fwd_fp8_outlier_workload_full_size():
+    # the GQA workload with outlier channels at its full size, in the launch
+    # configuration the FP8 benchmark times; sampled heads and rows
+    import torch
+    w = WORKLOADS["fwd_bf16_causal_gqa_b4_hq32_hkv8_n4096_d128_outliers"]
+    announce(f"fa_fwd_fp8 full size {w.name}")
+    inp = gen(w.seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim,
+              outliers=w.n_outlier_channels)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(w.seed, w.head_dim)
+    sd = _signs_dev(signs)
+    qc, qs = binding.quantize_fp8(q, sd)
+    kc, ks = binding.quantize_fp8(k, sd)
+    o, lse = binding.forward_fp8(qc, qs, kc, ks, v, w.scale, w.causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = host(o), host(lse)
+    rng = np.random.default_rng(99)
+    G = w.group
+    worst_o = worst_l = 0.0
+    for b, h in [(0, 0), (1, 9), (3, w.n_q_heads - 1)]:
+        g = h // G
+        oqc, oqs = ofp8.quantize(inp.q[b, h], signs)
+        okc, oks = ofp8.quantize(inp.k[b, g], signs)
+        np.testing.assert_array_equal(qc[b, h].cpu().numpy(), oqc)
+        np.testing.assert_array_equal(kc[b, g].cpu().numpy(), okc)
+        np.testing.assert_array_equal(qs[b, h].cpu().numpy(), oqs.astype(np.float32))
+        rows = _sample_rows(rng, w.seqlen, 48)
+        Or, Lr = oracle.forward_head(ofp8.dequantize(oqc, oqs), ofp8.dequantize(okc, oks), inp.v[b, g], w.scale,
+                                     w.causal, rows=rows)
+        bound = window_bound(oqc, oqs, okc, oks, w.scale, w.causal, rows)
+        _assert_within(O[b, h][rows], L[b, h][rows], Or, Lr, np.max(np.abs(inp.v[b, g])), bound, f"head {(b, h)}")
+        worst_o = max(worst_o, np.max(np.abs(O[b, h][rows] - Or)))
+        worst_l = max(worst_l, np.max(np.abs(L[b, h][rows] - Lr)))
+    print(f"{w.name} fp8: max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+
+
+def test_fwd_fp8_incoherent_processing_lowers_the_error():
+    # N(0,1) Q, K, V with 0.1% of the entries scaled by 30; the error of the
+    # FP8 forward against exact attention, with and without the transform
+    import torch
+    rng = np.random.default_rng(6)
+    shape = (1, 4, 512, 128)
+
+    def draw():
+        x = rng.standard_normal(shape).astype(np.float32)
+        x[rng.random(shape) < 0.001] *= np.float32(30.0)
+        return round_to_bf16(x)[0]
+
+    qh, kh, vh = draw(), draw(), draw()
+    q, k, v = _bf16_dev(qh), _bf16_dev(kh), _bf16_dev(vh)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    O_exact, _ = oracle.forward(qh, kh, vh, scale, False)
+    errs = {}
+    for name, signs in (("plain", None), ("hadamard", make_signs(17, 128))):
+        announce(f"fa_fwd_fp8 outlier error, {name}")
+        sd = _signs_dev(signs)
+        qc, qs = binding.quantize_fp8(q, sd)
+        kc, ks = binding.quantize_fp8(k, sd)
+        o, _ = binding.forward_fp8(qc, qs, kc, ks, v, scale, False, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        errs[name] = float(np.sqrt(np.mean((host(o) - O_exact) ** 2)))
+    print(f"rmse plain={errs['plain']:.4e} hadamard={errs['hadamard']:.4e} ratio={errs['plain'] / errs['hadamard']:.3f}")
+    assert errs["hadamard"] < errs["plain"]
