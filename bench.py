@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
     p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
+    p.add_argument("--persistent", action="store_true",
+                   help="time fa_fwd_persistent beside fa_fwd (default forward workload, or --workload)")
     p.add_argument("--fp8", action="store_true",
                    help="time fa_quantize_fp8 (Q and K) + fa_fwd_fp8 beside fa_fwd (default workload, or --workload)")
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
@@ -202,6 +204,33 @@ def bench_varlen(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_persistent(args):
+    """Time fa_fwd_persistent (work-queue grid) and fa_fwd (one workgroup per
+    item) on the same forward workload; prints one JSON line."""
+    import torch
+    w = WORKLOADS[args.workload or STEP_WORKLOAD]
+    if w.passes != "fwd" or w.dtype != "bf16":
+        raise SystemExit(f"--persistent needs a bf16 forward workload, not {w.name}")
+    _, q, k, v, _ = device_inputs(w, with_do=False)
+    step = Step(w, q, k, v, q)
+    sched = binding.new_sched()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def persist():
+        binding.forward_persistent(q, k, v, w.scale, w.causal, sched, o=o, lse=lse, stream=stream)
+
+    _, per_call, _ = time_calls(None, [persist, step.fwd], args.steps, args.warmup)
+    med = [float(np.median(per_call[:, i])) for i in range(2)]
+    ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    out = {"workload": f"{w.name}: fa_fwd_persistent vs fa_fwd", "persistent_ms": round(med[0], 4),
+           "persistent_tflops": round(ff / (med[0] * 1e-3) / 1e12, 2), "fa_fwd_ms": round(med[1], 4),
+           "fa_fwd_tflops": round(ff / (med[1] * 1e-3) / 1e12, 2),
+           "persistent_pct_of_bf16_peak": round(100 * ff / (med[0] * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2)}
+    print(json.dumps(out), flush=True)
+
+
 MI355X_FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA
 
 
@@ -290,12 +319,17 @@ def _template_args(kernel):
 
 def _call_of(kernel):
     t = _template_args(kernel)
-    # variable-length instances carry a trailing VARLEN = true argument
-    if ((kernel.startswith("void fa::fwd_kernel<") and len(t) == 6)
-            or (kernel.startswith("void fa::bwd_dkdv_kernel<") and len(t) == 4)
+    # fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>: the
+    # variable-length and persistent instances set VARLEN / PERSIST
+    if kernel.startswith("void fa::fwd_kernel<") and len(t) >= 6:
+        if t[5] == "true":
+            return "fa_fwd_varlen"
+        if len(t) >= 7 and t[6] == "true":
+            return "fa_fwd_persistent"
+    if ((kernel.startswith("void fa::bwd_dkdv_kernel<") and len(t) == 4)
             or (kernel.startswith("void fa::bwd_dq_kernel<") and len(t) == 3)):
         if t[-1] == "true":
-            return "fa_fwd_varlen" if "fwd_kernel" in kernel else "fa_bwd_varlen"
+            return "fa_bwd_varlen"
     if "bwd_preprocess_kernel" in kernel:
         zero_dq = kernel.rstrip().endswith(", true>(fa::BwdArgs)") or "Lb1EEEv" in kernel or ", true>" in kernel
         return "fa_bwd_atomic" if zero_dq else "fa_bwd"
@@ -443,6 +477,8 @@ def main():
 
     if args.fp8:
         return bench_fp8(args)
+    if args.persistent:
+        return bench_persistent(args)
     if args.workload:
         return bench_one(args)
     if args.varlen:

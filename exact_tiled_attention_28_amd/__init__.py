@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     fa_fp8_scales_count,
     fa_fwd,
     fa_fwd_fp8,
+    fa_fwd_persistent,
+    fa_fwd_persistent_sched_bytes,
     fa_fwd_varlen,
     fa_last_error,
     fa_quantize_fp8,
@@ -29,7 +31,9 @@ from .binding import (  # noqa: F401
     fa_version,
     forward,
     forward_fp8,
+    forward_persistent,
     forward_varlen,
     load_library,
+    new_sched,
     quantize_fp8,
 )

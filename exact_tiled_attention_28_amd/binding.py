@@ -67,6 +67,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if hasattr(lib, "fa_bwd_varlen"):
         lib.fa_bwd_varlen.restype = _c_int
         lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+    if hasattr(lib, "fa_fwd_persistent"):
+        lib.fa_fwd_persistent.restype = _c_int
+        lib.fa_fwd_persistent.argtypes = [_c_ptr] * 6 + [_c_int] * 6 + [_c_float] + [_c_int] * 3 + [_c_ptr]
+        lib.fa_fwd_persistent_sched_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_persistent_sched_bytes.argtypes = []
     if hasattr(lib, "fa_quantize_fp8"):
         lib.fa_quantize_fp8.restype = _c_int
         lib.fa_quantize_fp8.argtypes = [_c_ptr] * 4 + [_c_int] * 5 + [_c_ptr]
@@ -123,6 +128,16 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batc
     return load_library().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch,
                                         max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim,
                                         scale, causal, in_dtype, o_dtype, grad_dtype, stream)
+
+
+def fa_fwd_persistent(q, k, v, o, lse, sched, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim, scale,
+                      causal, in_dtype, out_dtype, stream) -> int:
+    return load_library().fa_fwd_persistent(q, k, v, o, lse, sched, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
+                                            head_dim, scale, causal, in_dtype, out_dtype, stream)
+
+
+def fa_fwd_persistent_sched_bytes() -> int:
+    return load_library().fa_fwd_persistent_sched_bytes()
 
 
 def fa_quantize_fp8(x, codes, block_scales, signs, batch, n_heads, seqlen, head_dim, in_dtype, stream) -> int:
@@ -319,4 +334,34 @@ def forward_fp8(q_codes, q_scales, k_codes, k_scales, v, scale, causal, out_dtyp
                     o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), oc,
                     _stream_handle(stream))
     _check(rc, "fa_fwd_fp8")
+    return o, lse
+
+
+def new_sched(device=None):
+    """A zeroed work-queue counter array for forward_persistent."""
+    import torch
+    return torch.zeros(fa_fwd_persistent_sched_bytes() // 4, dtype=torch.int32, device=device or "cuda")
+
+
+def forward_persistent(q, k, v, scale, causal, sched, out_dtype=None, o=None, lse=None, stream=None):
+    """forward() on the persistent work-queue grid; sched from new_sched()."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    oc = _dtype_code(q) if out_dtype is None else (FA_DTYPE_F32 if out_dtype == torch.float32 else FA_DTYPE_BF16)
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse, sched):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if sched.dtype != torch.int32 or sched.numel() * 4 < fa_fwd_persistent_sched_bytes():
+        raise TypeError("sched must be an int32 tensor from new_sched()")
+    rc = fa_fwd_persistent(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sched.data_ptr(),
+                           B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q), oc,
+                           _stream_handle(stream))
+    _check(rc, "fa_fwd_persistent")
     return o, lse

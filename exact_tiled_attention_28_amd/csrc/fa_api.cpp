@@ -51,6 +51,36 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(e, "fa_fwd launch");
 }
 
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse, int* sched, int batch,
+                      int n_q_heads, int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale,
+                      int causal, int in_dtype, int out_dtype, void* stream) {
+  std::string err;
+  const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
+  if (int rc = fa::check_fwd(q, k, v, o, lse, s, scale, causal, in_dtype, out_dtype, err)) return fail(rc, err);
+  if (sched == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "sched is NULL");
+  if (reinterpret_cast<uintptr_t>(sched) & 3u) return fail(FA_ERR_INVALID_ARGUMENT, "sched is not 4-byte aligned");
+  if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the persistent forward takes bf16 q, k, v");
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  a.sched = sched;
+  hipError_t e = fa::launch_fwd_persistent(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  return hip_status(e, "fa_fwd_persistent launch");
+}
+
+size_t fa_fwd_persistent_sched_bytes(void) { return 9 * sizeof(int); }
+
 }  // extern "C"
 
 static int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -26,6 +26,9 @@ struct FwdArgs {
   // of each 64-row block, [B][Hq][ceil(Nq/64)] and [B][Hkv][ceil(Nk/64)].
   const float* q_scales;
   const float* k_scales;
+  // Persistent forward (fa_fwd_persistent): 9 work-queue counters, zero on
+  // entry and left zero on exit.
+  int* sched;
 };
 
 struct BwdArgs {
@@ -52,6 +55,7 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool in_f32, bool causal, 
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
                       hipStream_t s);
 hipError_t launch_fwd_varlen(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
+hipError_t launch_fwd_persistent(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
                                int N, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, bool out_f32, hipStream_t s);

@@ -231,6 +231,29 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes,
                int seqlen_k, int head_dim, float scale, int causal,
                int out_dtype, void* stream);
 
+/*
+ * fa_fwd_persistent — fa_fwd (bf16 q, k, v) on a persistent grid fed by a
+ * work queue: the causal scheduler of the FlashAttention-3 news page
+ * ("persistent kernel"). As many workgroups as the device keeps resident
+ * pull (batch, query head, Q tile) items, heaviest causal tile first, from
+ * per-XCD queues, and take the lightest remaining items of the other queues
+ * when their own is empty. Results are bit-identical to fa_fwd's 4-wavefront
+ * kernel for the same inputs (the same per-item arithmetic).
+ *   sched  device int array of fa_fwd_persistent_sched_bytes() bytes,
+ *          4-byte aligned, all zero before the first call; every call leaves
+ *          it zero when it completes. Calls that may run at the same time
+ *          (different streams) need separate arrays.
+ *   other arguments as in fa_fwd; in_dtype must be FA_DTYPE_BF16.
+ */
+int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int* sched, int batch, int n_q_heads,
+                      int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim,
+                      float scale, int causal, int in_dtype, int out_dtype,
+                      void* stream);
+
+/* Bytes of the work-queue counter array fa_fwd_persistent needs (36). */
+size_t fa_fwd_persistent_sched_bytes(void);
+
 /* Bytes of device workspace fa_bwd and fa_bwd_atomic need: 4 * batch * n_q_heads * seqlen_q
  * (the fp32 vector D, page 6.2 section 7.3). Returns 0 for non-positive
  * arguments. */

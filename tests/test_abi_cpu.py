@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["fa_bwd", "fa_bwd_atomic", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count", "fa_fwd",
-         "fa_fwd_fp8", "fa_fwd_varlen", "fa_last_error", "fa_quantize_fp8", "fa_status_string", "fa_version"])
+         "fa_fwd_fp8", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes", "fa_fwd_varlen", "fa_last_error",
+         "fa_quantize_fp8", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -192,6 +193,34 @@ def test_varlen_without_query_rows_launches_nothing(lib):
     # max_seqlen_q == 0: nothing to compute; the call succeeds without a GPU
     # launch (the fake pointers are never touched).
     assert fwd_varlen(max_q=0, total_q=0) == 0
+
+
+def fwd_persistent(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, sched=CU, batch=1, n_q_heads=2, n_kv_heads=1, seqlen_q=16, seqlen_k=16,
+                head_dim=64, scale=0.125, causal=0, in_dtype=1, out_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_fwd_persistent(*args.values())
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(o=MIS), INVALID, "o is not 16-byte aligned"),
+    (dict(sched=0), INVALID, "sched is NULL"),
+    (dict(sched=CU_MIS), INVALID, "sched is not 4-byte aligned"),
+    (dict(batch=0), INVALID, "sizes must be >= 1"),
+    (dict(n_q_heads=3, n_kv_heads=2), INVALID, "multiple of n_kv_heads"),
+    (dict(causal=1, seqlen_k=17), UNSUP, "seqlen_q == seqlen_k"),
+    (dict(in_dtype=0), UNSUP, "bf16"),
+    (dict(out_dtype=5), INVALID, "FA_DTYPE"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
+])
+def test_fwd_persistent_argument_errors(lib, kw, code, text):
+    assert fwd_persistent(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+def test_fwd_persistent_sched_bytes(lib):
+    assert binding.fa_fwd_persistent_sched_bytes() == 36
 
 
 def quantize_fp8(**kw):

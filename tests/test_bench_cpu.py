@@ -39,6 +39,10 @@ def test_kernel_to_entry_point():
     assert bench._call_of("__amd_rocclr_copyBuffer") is None
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, true>(fa::FwdArgs)") == "fa_fwd_varlen"
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false>(fa::FwdArgs)") == "fa_fwd"
+    assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false, false>(fa::FwdArgs)") == "fa_fwd"
+    assert bench._call_of("void fa::fwd_kernel<false, 64, true, true, 4, true, false>(fa::FwdArgs)") == "fa_fwd_varlen"
+    assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false, true>(fa::FwdArgs)") \
+        == "fa_fwd_persistent"
     assert bench._call_of("void fa::bwd_dkdv_kernel<128, true, false, true>(fa::BwdArgs)") == "fa_bwd_varlen"
     assert bench._call_of("void fa::bwd_dq_kernel<128, true, true>(fa::BwdArgs)") == "fa_bwd_varlen"
     assert bench._call_of("void fa::bwd_dq_kernel<128, true, false>(fa::BwdArgs)") == "fa_bwd"
