@@ -410,43 +410,46 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 //
 // Same method as bwd_kernel without dQ. The workgroup owns a K/V column block
-// of 128 keys; wavefront w takes keys 32*(w%4).. and query rows
-// 32*(w/4).. of every 64-row Q block, so each wavefront does 32 x 32 per
-// step and only 32 keys' dK, dV accumulate in its registers. K_j and V_j are
-// read from LDS as B operands (not held in registers), which keeps a
-// wavefront under 256 registers (2 per SIMD) with dK, dV in accumulation
-// registers. The two wavefronts that share keys sum their dK, dV through LDS
-// once at the end.
+// of 128 keys and walks every Q block of 64 rows (of every query head of the
+// group) that can see it. Wavefront w = (kg, h), kg = w mod 4, h = w / 4,
+// owns the 32 keys 32*kg.. of the block: their K and V rows stay in its
+// registers for the whole loop as the B operands of S = Q K^T and
+// dP = dO V^T, which it forms for the 32 query rows 32*h.. of each Q block.
+// Its dK, dV accumulators cover only head-dim half h (32 keys x D/2 each).
+// The two wavefronts with the same keys swap their P and dS (bf16, exactly
+// the registers that feed the products) through LDS once per Q block, so each
+// adds all 64 query rows to its half of dV^T += dO^T P and dK^T += Q^T dS.
+// Compared with each wavefront accumulating the full head dimension for its
+// own 32 query rows and summing the halves at the end, this halves the
+// accumulator registers, which pays for K and V in registers (no K/V operand
+// reads from LDS) and leaves room for the scheduler.
 template <int D>
 struct DkdvTile {
   static constexpr int NW = 8;
   static constexpr int BKV = 128, BQ = 64;
   static constexpr int ROWB = D * 2, RC = ROWB / 16;
-  static constexpr int QTILEB = BQ * ROWB, KTILEB = BKV * ROWB;
+  static constexpr int QTILEB = BQ * ROWB;
   static constexpr int QCPW = QTILEB / (1024 * NW);
-  static constexpr int KCPT = BKV * RC / (64 * NW);
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_V = OFF_K + KTILEB;
-  static constexpr int OFF_Q = OFF_V + KTILEB;        // [2][QTILEB]
+  static constexpr int XB = 4 * 64 * 16;              // per wavefront: P and dS, 2 x bf16x8 each per lane
+  static constexpr int OFF_X = 0;                     // [NW][XB]
+  static constexpr int OFF_Q = OFF_X + NW * XB;       // [2][QTILEB]
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;   // [2][QTILEB]
   static constexpr int OFF_L = OFF_DO + 2 * QTILEB;   // [2][BQ]
   static constexpr int OFF_D = OFF_L + 2 * BQ * 4;    // [2][BQ]
   static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
-  static constexpr int RED_BYTES = 4 * (D / 32) * 16 * 64 * 4;  // one accumulator of the 4 key groups
-  static_assert(QTILEB % (1024 * NW) == 0 && (BKV * RC) % (64 * NW) == 0, "tiles must split evenly");
-  static_assert(RED_BYTES <= 4 * QTILEB, "the reduction buffer reuses the Q / dO tiles");
+  static_assert(QTILEB % (1024 * NW) == 0, "tiles must split evenly");
+  static_assert(D % 64 == 0, "each wavefront takes whole 32-wide head-dim blocks of one half");
 };
 
 template <int D, bool CAUSAL, bool GF32, bool VARLEN = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdArgs a) {
   using T = DkdvTile<D>;
   constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB;
-  constexpr int QCPW = T::QCPW, KCPT = T::KCPT;
-  constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int QCPW = T::QCPW, XB = T::XB;
+  constexpr int NKK = D / 16, NDH = D / 64;  // NDH: 32-wide head-dim blocks per half
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const sK = smem + T::OFF_K;
-  char* const sV = smem + T::OFF_V;
+  char* const sX = smem + T::OFF_X;
   char* const sQ = smem + T::OFF_Q;
   char* const sDO = smem + T::OFF_DO;
   float* const sL = (float*)(smem + T::OFF_L);
@@ -455,8 +458,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int kg = w & 3;   // key group: keys 32*kg.. of the block
-  const int qh = w >> 2;  // query half: rows 32*qh.. of each Q block
+  const int kg = w & 3;  // key group: keys 32*kg.. of the block
+  const int h = w >> 2;  // query half for S and dP, head-dim half for dK and dV
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int j16 = lane & 15;
@@ -488,39 +491,42 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (VARLEN) return (size_t)hq * a.total_q + q_off;
     return (size_t)(b * a.Hq + hq) * a.Nq;
   };
-  const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
-  const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
 
-  // K_j and V_j tiles (rows past the end are zero).
+  // K and V rows of this lane's key as B operands: head-dim elements
+  // 16*kk + 8*g .. +7 (zero past the end of K/V).
+  bf16x8 kf[NKK], vf[NKK];
+  {
+    const bool ok = key < Nk;
+    const size_t row = (kvhead + (ok ? key : 0)) * ROWB;
+    const char* Kr = (const char*)a.k + row;
+    const char* Vr = (const char*)a.v + row;
 #pragma unroll
-  for (int u = 0; u < KCPT; ++u) {
-    const int ci = tid + 64 * T::NW * u;
-    const int row = ci / RC, cc = ci % RC;
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (kv0 + row < Nk) {
-      const size_t off = (size_t)(kv0 + row) * ROWB + cc * 16;
-      x = *(const u32x4*)(Kh + off);
-      y = *(const u32x4*)(Vh + off);
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (ok) {
+        x = *(const u32x4*)(Kr + (kk * 16 + 8 * g) * 2);
+        y = *(const u32x4*)(Vr + (kk * 16 + 8 * g) * 2);
+      }
+      kf[kk] = __builtin_bit_cast(bf16x8, x);
+      vf[kk] = __builtin_bit_cast(bf16x8, y);
     }
-    const int lo = tile_off<RC>(row, cc * 16);
-    *(u32x4*)(sK + lo) = x;
-    *(u32x4*)(sV + lo) = y;
   }
 
-  // Per-lane LDS offsets (row swizzles repeat every 8 rows).
+  // Per-lane LDS offsets.
   int roff[NKK];  // row reads: row l32 of a 32-row block, head-dim step kk
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) roff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
-  int troff[NDB][2];  // transpose reads: column block db, half h
+  int troff[NDH][2];  // transpose reads: this wavefront's head-dim blocks, half hh
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDH; ++db)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      troff[db][h] = tile_off<RC>(4 * g + 8 * h + (j16 >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
+    for (int hh = 0; hh < 2; ++hh)
+      troff[db][hh] = tile_off<RC>(4 * g + 8 * hh + (j16 >> 2),
+                                   ((h * NDH + db) * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
 
-  f32x16 dkacc[NDB], dvacc[NDB];
+  f32x16 dkacc[NDH], dvacc[NDH];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDH; ++db) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
@@ -571,23 +577,23 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   wait_vmem();
   __syncthreads();
 
-  const char* const kTile = sK + kg * 32 * ROWB;
-  const char* const vTile = sV + kg * 32 * ROWB;
+  char* const myX = sX + w * XB;
+  const char* const ptX = sX + (w ^ 4) * XB;
 
-  auto body = [&](auto mask_tag, int q0, const char* tQ, const char* tDO, const float* tL, const float* tD)
-      __attribute__((always_inline)) {
+  // P and dS of this wavefront's 32 x 32 block (keys x its query half).
+  auto scores = [&](auto mask_tag, int q0, const char* tQ, const char* tDO, const float* tL, const float* tD,
+                    bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* qRows = tQ + qh * 32 * ROWB;
-    const char* oRows = tDO + qh * 32 * ROWB;
-    // S = Q K^T (query rows in registers, one key per lane)
+    const char* qRows = tQ + h * 32 * ROWB;
+    const char* oRows = tDO + h * 32 * ROWB;
+    // S = Q K^T (query rows from LDS, K rows in registers, one key per lane)
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      s = mfma_bf16(*(const bf16x8*)(qRows + roff[kk]), *(const bf16x8*)(kTile + roff[kk]), s);
+    for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16(*(const bf16x8*)(qRows + roff[kk]), kf[kk], s);
     // P = exp2(S c - L log2 e)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const int r0 = qh * 32 + 8 * a4 + 4 * g;
+      const int r0 = h * 32 + 8 * a4 + 4 * g;
       const f32x4 lv = *(const f32x4*)(tL + r0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -599,7 +605,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         s[4 * a4 + e] = p;
       }
     }
-    bf16x8 pb[2];
     {
       float pv[8];
 #pragma unroll
@@ -609,39 +614,39 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         pb[t] = to_bf16x8(pv);
       }
     }
-    // dV^T += dO^T P over this wave's 32 query rows (two 16-row steps)
+    // dP = dO V^T, dS = P o (dP - D)
+    f32x16 dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) dp = mfma_bf16(*(const bf16x8*)(oRows + roff[kk]), vf[kk], dp);
+    float dsv[16];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const f32x4 dv = *(const f32x4*)(tD + h * 32 + 8 * a4 + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsv[4 * a4 + e] = s[4 * a4 + e] * (dp[4 * a4 + e] - dv[e]);
+    }
+    dsb[0] = to_bf16x8(dsv);
+    dsb[1] = to_bf16x8(dsv + 8);
+  };
+
+  // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of half hh, for
+  // this wavefront's head-dim half.
+  auto grads = [&](int hh, const char* tQ, const char* tDO, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const char* base = oRows + 16 * t * ROWB;
+      for (int db = 0; db < NDH; ++db) {
+        const char* base = tDO + (32 * hh + 16 * t) * ROWB;
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
         dvacc[db] = mfma_bf16(cat4(lo, hi), pb[t], dvacc[db]);
       }
-    // dP = dO V^T, dS = P o (dP - D)
-    f32x16 dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      dp = mfma_bf16(*(const bf16x8*)(oRows + roff[kk]), *(const bf16x8*)(vTile + roff[kk]), dp);
-    bf16x8 dsb[2];
-    {
-      float dsv[16];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 dv = *(const f32x4*)(tD + qh * 32 + 8 * a4 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsv[4 * a4 + e] = s[4 * a4 + e] * (dp[4 * a4 + e] - dv[e]);
-      }
-      dsb[0] = to_bf16x8(dsv);
-      dsb[1] = to_bf16x8(dsv + 8);
-    }
-    // dK^T += Q^T dS
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const char* base = qRows + 16 * t * ROWB;
+      for (int db = 0; db < NDH; ++db) {
+        const char* base = tQ + (32 * hh + 16 * t) * ROWB;
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
         dkacc[db] = mfma_bf16(cat4(lo, hi), dsb[t], dkacc[db]);
@@ -658,54 +663,46 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const char* tDO = sDO + buf * QTILEB;
     const float* tL = sL + buf * BQ;
     const float* tD = sD + buf * BQ;
-    // Skip when all of this wavefront's keys lie after all of its queries.
-    const bool active = !CAUSAL || kv0 + 32 * kg <= q0 + 32 * qh + 31;
-    if (active) {
-      const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * qh) || (kv0 + 32 * kg + 32 > Nk);
+    // A (key group, query half) block is skipped when all its keys lie after
+    // all its queries.
+    const bool act0 = !CAUSAL || kv0 + 32 * kg <= q0 + 31;
+    const bool act1 = !CAUSAL || kv0 + 32 * kg <= q0 + 63;
+    const bool mine = h ? act1 : act0;
+    bf16x8 pb[2] = {}, dsb[2] = {};
+    if (mine) {
+      const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * h) || (kv0 + 32 * kg + 32 > Nk);
       if (need_mask)
-        body(std::true_type{}, q0, tQ, tDO, tL, tD);
+        scores(std::true_type{}, q0, tQ, tDO, tL, tD, pb, dsb);
       else
-        body(std::false_type{}, q0, tQ, tDO, tL, tD);
+        scores(std::false_type{}, q0, tQ, tDO, tL, tD, pb, dsb);
+      *(bf16x8*)(myX + (0 * 64 + lane) * 16) = pb[0];
+      *(bf16x8*)(myX + (1 * 64 + lane) * 16) = pb[1];
+      *(bf16x8*)(myX + (2 * 64 + lane) * 16) = dsb[0];
+      *(bf16x8*)(myX + (3 * 64 + lane) * 16) = dsb[1];
+    }
+    __syncthreads();
+    if (mine) grads(h, tQ, tDO, pb, dsb);
+    if (h ? act0 : act1) {
+      bf16x8 ppb[2], pds[2];
+      ppb[0] = *(const bf16x8*)(ptX + (0 * 64 + lane) * 16);
+      ppb[1] = *(const bf16x8*)(ptX + (1 * 64 + lane) * 16);
+      pds[0] = *(const bf16x8*)(ptX + (2 * 64 + lane) * 16);
+      pds[1] = *(const bf16x8*)(ptX + (3 * 64 + lane) * 16);
+      grads(h ^ 1, tQ, tDO, ppb, pds);
     }
     if (has_next) store_ld(buf ^ 1);
     wait_vmem();
     __syncthreads();
   }
 
-  // ---- sum the two query halves' dK, dV through LDS, then store ------------
-  f32x4* red = (f32x4*)sQ;  // [kg][db][r/4][lane], reuses the Q / dO tiles
-  auto exchange = [&](f32x16 (&acc)[NDB]) __attribute__((always_inline)) {
-    if (qh == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-          red[((kg * NDB + db) * 4 + a4) * 64 + lane] =
-              f32x4{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
-    }
-    __syncthreads();
-    if (qh == 0) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 x = red[((kg * NDB + db) * 4 + a4) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[db][4 * a4 + e] += x[e];
-        }
-    }
-    __syncthreads();
-  };
-  exchange(dkacc);
-  exchange(dvacc);
-
-  if (qh == 0 && key < Nk) {
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T for this head-dim half --------
+  if (key < Nk) {
     const size_t rowoff = (kvhead + key) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDH; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int d0 = db * 32 + 8 * a4 + 4 * g;
+        const int d0 = (h * NDH + db) * 32 + 8 * a4 + 4 * g;
         const f32x4 kv = {scale * dkacc[db][4 * a4], scale * dkacc[db][4 * a4 + 1], scale * dkacc[db][4 * a4 + 2],
                           scale * dkacc[db][4 * a4 + 3]};
         const f32x4 vv = {dvacc[db][4 * a4], dvacc[db][4 * a4 + 1], dvacc[db][4 * a4 + 2], dvacc[db][4 * a4 + 3]};
