@@ -1,0 +1,19 @@
+"""Build the test helper tests/hw/libfp8probe.so (gfx950) from
+fp8_mfma_probe.hip; called by the repository's build entry point."""
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "fp8_mfma_probe.hip")
+LIB = os.path.join(HERE, "libfp8probe.so")
+
+
+def build() -> str:
+    from exact_tiled_attention_28_amd.build import hipcc
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the FP8 probe failed:\n" + res.stdout + res.stderr)
+    return LIB

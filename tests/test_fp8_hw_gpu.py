@@ -1,0 +1,98 @@
+"""The accumulation property of the FP8 matrix instruction that the FP8
+forward's parity bound rests on (tests/test_fp8_gpu.py): one
+v_mfma_f32_32x32x64_f8f6f4 adds its 64 exact e4m3 x e4m3 products in a
+window anchored at the largest product, so every term is off by less than
+2^(E - 12), E = floor(log2 max |product|), and the sum is then added to the
+fp32 accumulator input with one fp32 rounding. Checked on targeted sums and
+on random codes of several magnitude mixes against exact float64 sums
+(products of two E4M3 values and their sums are exact in float64 here).
+Uses the test helper tests/hw/libfp8probe.so.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle.fp8 import e4m3_decode
+from tests.gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hw", "libfp8probe.so")
+CASE = np.dtype([("a", np.uint8, 64), ("b", np.uint8, 64), ("c", np.float32)])
+
+
+def _probe(cases):
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.fp8_dot_probe.restype = ctypes.c_int
+    lib.fp8_dot_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.fp8_dot_probe_case_bytes.restype = ctypes.c_int
+    assert lib.fp8_dot_probe_case_bytes() == CASE.itemsize
+    raw = torch.from_numpy(np.frombuffer(cases.tobytes(), dtype=np.uint8).copy()).cuda()
+    out = torch.empty(len(cases), dtype=torch.float32, device="cuda")
+    rc = lib.fp8_dot_probe(raw.data_ptr(), out.data_ptr(), len(cases), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _p2(k):
+    """E4M3 code of 2^k, k in [-9, 8]."""
+    return (k + 7) << 3 if k >= -6 else 1 << (k + 9)
+
+
+def _cases():
+    out = []
+
+    def add(pairs, c=0.0):
+        x = np.zeros(1, CASE)
+        for i, (p, q) in enumerate(pairs):
+            x["a"][0, i], x["b"][0, i] = p, q
+        x["c"][0] = c
+        out.append(x)
+
+    for k in range(1, 19):  # 1 + 2^-k
+        add([(_p2(0), _p2(0)), (_p2(-(k // 2)), _p2(-(k - k // 2)))])
+    add([(0x7E, 0x7E), (_p2(0), _p2(0))])                                   # 448^2 + 1
+    add([(_p2(8), _p2(0)), (_p2(8), 0x80 | _p2(0)), (_p2(-9), _p2(-9))])    # 256 - 256 + 2^-18
+    add([(_p2(-9), _p2(-9))], c=1.0)                                         # C = 1, + 2^-18
+    add([(_p2(0), _p2(0))], c=2.0 ** 20)                                     # C = 2^20, + 1
+    rng = np.random.default_rng(2)
+    for mode in range(4):
+        x = np.zeros(100, CASE)
+        for n in range(100):
+            codes = rng.integers(0, 256, size=128).astype(np.uint8)
+            codes = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes)  # no NaN codes
+            if mode == 1:
+                codes = (codes & 0x80) | ((codes & 0x7F) % 0x40)             # magnitudes below 2
+            if mode == 2:
+                small = rng.random(128) < 63 / 64
+                codes = np.where(small, (codes & 0x80) | (0x08 + (codes & 0x1F)), codes)  # rare large terms
+            x["a"][n], x["b"][n] = codes[:64], codes[64:]
+            if mode == 3:
+                x["c"][n] = np.float32(np.ldexp(float(rng.integers(-1000, 1001)), int(rng.integers(0, 20))))
+        out.append(x)
+    return np.concatenate(out)
+
+
+def test_fp8_instruction_error_is_within_the_window_bound():
+    cases = _cases()
+    announce(f"fp8 dot probe, {len(cases)} cases")
+    got = _probe(cases)
+    prods = e4m3_decode(cases["a"]) * e4m3_decode(cases["b"])
+    exact = prods.sum(axis=1) + cases["c"].astype(np.float64)
+    absmax = np.abs(prods).max(axis=1)
+    nz = (prods != 0).sum(axis=1)
+    E = np.floor(np.log2(np.where(absmax > 0, absmax, 1.0)))
+    bound = np.where(absmax > 0, nz * np.exp2(E - 12), 0.0) + np.abs(exact) * 2.0 ** -23
+    err = np.abs(got - exact)
+    worst = int(np.argmax(err / np.maximum(bound, 1e-300)))
+    print(f"max err / bound = {err[worst] / max(bound[worst], 1e-300):.3f} (case {worst})")
+    assert np.all(err <= bound), f"case {worst}: got {got[worst]!r}, exact {exact[worst]!r}"
+    # the targeted sums: the window keeps at least 12 bits below the largest product
+    for k in range(1, 13):
+        assert got[k - 1] == 1.0 + 2.0 ** -k
+    assert got[20] == 1.0 + 2.0 ** -18 and got[21] == 2.0 ** 20 + 1
