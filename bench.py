@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
     p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
+    p.add_argument("--sweep", action="store_true",
+                   help="fa_fwd / fa_bwd throughput over head dim 64/128, N 1K-32K, causal and not, MHA and GQA")
     p.add_argument("--persistent", action="store_true",
                    help="time fa_fwd_persistent beside fa_fwd (default forward workload, or --workload)")
     p.add_argument("--fp8", action="store_true",
@@ -202,6 +204,66 @@ def bench_varlen(args):
     out["fwd_pct_of_bf16_peak"] = round(100 * out["fwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 2)
     out["bwd_pct_of_bf16_peak"] = round(100 * out["bwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 2)
     print(json.dumps(out), flush=True)
+
+
+SWEEP_TOKENS, SWEEP_HD = 16384, 2048  # B * N tokens and Hq * d per shape
+
+
+def bench_sweep(args):
+    """Throughput of fa_fwd (bf16 O) and fa_bwd (fp32 dQ, bf16 dK/dV) over
+    head dim 64/128, N = 1K..32K, causal and non-causal, MHA and GQA (G = 4),
+    with B = max(1, 16384 / N) and Hq = 2048 / d: N(0, 1) bf16 inputs drawn on
+    the GPU from a seeded generator. One JSON line per shape (median of
+    --steps timed calls after --warmup), then a summary line."""
+    import torch
+    rows = []
+    for d in (64, 128):
+        for n in (1024, 2048, 4096, 8192, 16384, 32768):
+            for causal in (True, False):
+                for group in (1, 4):
+                    B, Hq = max(1, SWEEP_TOKENS // n), SWEEP_HD // d
+                    Hkv = Hq // group
+                    g = torch.Generator(device="cuda").manual_seed(1000 + n + d + group)
+                    q = torch.randn(B, Hq, n, d, device="cuda", generator=g).bfloat16()
+                    k = torch.randn(B, Hkv, n, d, device="cuda", generator=g).bfloat16()
+                    v = torch.randn(B, Hkv, n, d, device="cuda", generator=g).bfloat16()
+                    do = torch.randn(B, Hq, n, d, device="cuda", generator=g).bfloat16()
+                    scale = float(np.float32(1 / np.sqrt(d)))
+                    o = torch.empty_like(q)
+                    lse = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+                    dq = torch.empty((B, Hq, n, d), dtype=torch.float32, device="cuda")
+                    dk, dv = torch.empty_like(k), torch.empty_like(v)
+                    ws = torch.empty(binding.fa_bwd_workspace_bytes(B, Hq, n) // 4, dtype=torch.float32,
+                                     device="cuda")
+                    sh = torch.cuda.current_stream().cuda_stream
+                    bf = binding.FA_DTYPE_BF16
+
+                    def fwd():
+                        rc = binding.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                            B, Hq, Hkv, n, n, d, scale, int(causal), bf, bf, sh)
+                        if rc:
+                            raise binding.FAError(rc, "fa_fwd", binding.fa_last_error())
+
+                    def bwd():
+                        rc = binding.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                            B, Hq, Hkv, n, n, d, scale, int(causal), bf, bf, bf, sh)
+                        if rc:
+                            raise binding.FAError(rc, "fa_bwd", binding.fa_last_error())
+
+                    _, per_call, _ = time_calls(None, [fwd, bwd], args.steps, args.warmup)
+                    fm, bm = float(np.median(per_call[:, 0])), float(np.median(per_call[:, 1]))
+                    ff, bfl = fwd_flops(B, Hq, n, n, d, causal), bwd_flops(B, Hq, n, n, d, causal)
+                    row = {"d": d, "N": n, "B": B, "Hq": Hq, "Hkv": Hkv, "causal": causal,
+                           "fwd_ms": round(fm, 4), "fwd_tflops": round(ff / (fm * 1e-3) / 1e12, 1),
+                           "bwd_ms": round(bm, 4), "bwd_tflops": round(bfl / (bm * 1e-3) / 1e12, 1)}
+                    row["fwd_pct"] = round(100 * row["fwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 1)
+                    row["bwd_pct"] = round(100 * row["bwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 1)
+                    rows.append(row)
+                    print(json.dumps(row), flush=True)
+                    del q, k, v, do, o, lse, dq, dk, dv, ws
+    best = max(rows, key=lambda r: r["fwd_tflops"] if r["causal"] and r["d"] == 128 else 0)
+    print(json.dumps({"sweep_shapes": len(rows), "best_causal_d128_fwd": best}), flush=True)
 
 
 def bench_persistent(args):
@@ -479,6 +541,8 @@ def main():
         return bench_fp8(args)
     if args.persistent:
         return bench_persistent(args)
+    if args.sweep:
+        return bench_sweep(args)
     if args.workload:
         return bench_one(args)
     if args.varlen:
