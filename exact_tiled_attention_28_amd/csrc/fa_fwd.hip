@@ -389,7 +389,7 @@ fwd_kernel(FwdArgs a) {
     run_item(blockIdx.x);
   } else {
     // Work queue (the persistent causal scheduler of the FlashAttention-3
-    // news page, "persistent kernel"): the grid holds only as many
+    // news page, on persistent kernels): the grid holds only as many
     // workgroups as stay resident, and each pulls items until none are
     // left. Item L lives in queue L mod 8, in increasing L, i.e. the same
     // heaviest-first order and the same XCD (workgroup b runs on XCD

@@ -234,7 +234,7 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes,
 /*
  * fa_fwd_persistent — fa_fwd (bf16 q, k, v) on a persistent grid fed by a
  * work queue: the causal scheduler of the FlashAttention-3 news page
- * ("persistent kernel"). As many workgroups as the device keeps resident
+ * (on persistent kernels). As many workgroups as the device keeps resident
  * pull (batch, query head, Q tile) items, heaviest causal tile first, from
  * per-XCD queues, and take the lightest remaining items of the other queues
  * when their own is empty. Results are bit-identical to fa_fwd's 4-wavefront
