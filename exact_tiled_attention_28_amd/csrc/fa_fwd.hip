@@ -714,16 +714,18 @@ static hipError_t launch_fwd_pp(FwdArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Key lengths from which the two-group (ping-pong) bf16 kernel is used. Its
-// 256-row Q tiles and two-phase pipeline pay a fill/drain cost per Q tile
-// that short key sequences do not amortise; measured on MI355X (same box):
-// N=2048 causal d=128: 4-wave kernel 0.215 ms vs 0.223 ms; N=4096 GQA:
-// 0.643 vs 0.631 ms; N=16384: 4-wave ~0.68 ms vs 0.60 ms.
+// The two-group (ping-pong) bf16 kernel is used for d = 128 without the
+// causal mask from this many keys on. Its 256-row Q tiles and two-phase
+// pipeline pay a fill/drain cost per Q tile; measured on MI355X against the
+// 4-wave kernel (one box, N = 4K..32K, MHA and GQA): d = 128 non-causal
+// 2-3 % faster; d = 128 causal 4 % slower at 4K and within +-1.6 % from 8K;
+// d = 64 4-16 % slower at every length, so the other cases keep the 4-wave
+// kernel.
 constexpr int kPingPongMinKeys = 4096;
 
 template <bool F32IN, int D, bool CAUSAL, bool OUTF32>
 static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
-  if constexpr (!F32IN) {
+  if constexpr (!F32IN && D == 128 && !CAUSAL) {
     if (a.Nk >= kPingPongMinKeys) return launch_fwd_pp<D, CAUSAL, OUTF32>(a, stream);
   }
   constexpr int NW = 4;
