@@ -67,95 +67,95 @@ __device__ __forceinline__ int block_scale_exp(float amax) {
 
 // ---------------------------------------------------------------------------
 // Quantize pass: one workgroup (4 wavefronts) per 64-row block of one head.
-// A row is spread over D/8 lanes holding 8 consecutive elements each, so the
-// butterflies of stages h < 8 stay inside a lane and stages h >= 8 exchange
-// with lane ^ (h / 8).
+// A row is spread over 4 lanes (a quad) holding D/4 consecutive elements
+// each, so the butterflies of stages h < D/4 stay inside a lane and only the
+// last two stages exchange values, with the lanes l ^ 1 and l ^ 2 of the same
+// quad. A wavefront covers 16 rows, the workgroup the 64 rows of the block.
+// (Measured at B8 H16 N2048 d128: 35 us per tensor, against 44 us with 16
+// lanes per row and 52 us with one wavefront per block.)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) quantize_fp8_kernel(const __bf16* __restrict__ x, uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales, const signed char* signs,
                                                             int N, int n_blocks) {
-  constexpr int LPR = D / 8;         // lanes per row
-  constexpr int RPP = 64 / LPR;      // rows per wavefront pass
-  constexpr int PASSES = 16 / RPP;   // each wavefront handles 16 rows of the block
+  constexpr int EPL = D / 4;  // elements per lane
+  constexpr int NV = EPL / 8;  // 16-byte loads per lane
   __shared__ float wmax[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = blockIdx.x / n_blocks, blk = blockIdx.x % n_blocks;
-  const int c0 = (lane % LPR) * 8;   // first element of this lane
+  const int q = lane & 3;      // position in the quad
+  const int c0 = q * EPL;      // first element of this lane
+  const int row = blk * 64 + w * 16 + (lane >> 2);
   const size_t head_off = (size_t)head * N * D;
 
-  float sg[8];
+  float v[EPL];
+  if (row < N) {
+    const __bf16* xr = x + head_off + (size_t)row * D + c0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sg[e] = signs ? (float)signs[c0 + e] : 1.0f;
-  const float inv_sqrt_d = D == 64 ? 0.125f : 0.08838834764831845f;
-
-  float y[PASSES][8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int row = blk * 64 + w * 16 + p * RPP + lane / LPR;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < N) {
-      const u32x4 raw = *(const u32x4*)(x + head_off + (size_t)row * D + c0);
+    for (int u = 0; u < NV; ++u) {
+      const u32x4 raw = *(const u32x4*)(xr + 8 * u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(raw[i] << 16);
-        v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+        v[8 * u + 2 * i] = __uint_as_float(raw[i] << 16);
+        v[8 * u + 2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
       }
     }
-    if (signs) {
+  } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= sg[e];
-      // stages h = 1, 2, 4 inside the lane
-#pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!(e & h)) {
-            const float a = v[e], b = v[e + h];
-            v[e] = a + b;
-            v[e + h] = a - b;
-          }
-      // stages h = 8 .. D/2 across lanes: the partner holds element c +- h
-#pragma unroll
-      for (int h = 8; h < D; h <<= 1) {
-        const int m = h / 8;
-        const bool lower = ((lane % LPR) & m) == 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float o = __shfl_xor(v[e], m, 64);
-          v[e] = lower ? v[e] + o : o - v[e];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= inv_sqrt_d;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[p][e] = v[e];
-      amax = fmaxf(amax, fabsf(v[e]));
-    }
+    for (int e = 0; e < EPL; ++e) v[e] = 0.0f;
   }
+  if (signs) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] *= (float)signs[c0 + e];
+    // stages h = 1 .. EPL/2 inside the lane
+#pragma unroll
+    for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        if (!(e & h)) {
+          const float a = v[e], b2 = v[e + h];
+          v[e] = a + b2;
+          v[e + h] = a - b2;
+        }
+    // stages h = EPL, 2 EPL across the quad: the partner holds element c +- h
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+      const bool lower = (q & m) == 0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float o = __shfl_xor(v[e], m, 64);
+        v[e] = lower ? v[e] + o : o - v[e];
+      }
+    }
+    const float inv_sqrt_d = D == 64 ? 0.125f : 0.08838834764831845f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] *= inv_sqrt_d;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[e]));
   // block max over the 4 wavefronts
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   if (lane == 0) wmax[w] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const int e = block_scale_exp(amax);
-  if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, e);
+  const int e2 = block_scale_exp(amax);
+  if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, e2);
+  if (row < N) {
+    uint8_t* cr = codes + head_off + (size_t)row * D + c0;
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int row = blk * 64 + w * 16 + p * RPP + lane / LPR;
-    if (row < N) {
-      unsigned lo = 0, hi = 0;
+    for (int u = 0; u < EPL / 16; ++u) {
+      u32x4 out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_code(ldexpf(y[p][i], -e)) << (8 * i);
-        hi |= e4m3_code(ldexpf(y[p][i + 4], -e)) << (8 * i);
+        unsigned word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(v[16 * u + 4 * i + j], -e2)) << (8 * j);
+        out[i] = word;
       }
-      *(u32x2*)(codes + head_off + (size_t)row * D + c0) = u32x2{lo, hi};
+      *(u32x4*)(cr + 16 * u) = out;
     }
   }
 }
