@@ -413,8 +413,8 @@ fwd_kernel(FwdArgs a) {
     auto fetch_now = [&]() __attribute__((always_inline)) {
       while (qs < 8) {
         const int x = (x0 + qs) & 7;
-        const int L = x + 8 * atomicAdd(&sched[x], 1);
-        if (L < total) return L;
+        const long long L = x + 8LL * atomicAdd(&sched[x], 1);
+        if (L >= 0 && L < total) return (int)L;  // out of range (or a counter that was not zero): queue done
         ++qs;
       }
       return -1;
@@ -433,8 +433,9 @@ fwd_kernel(FwdArgs a) {
       if (tid == 0) {
         int nl = -1;
         if (qs < 8) {
-          nl = ((x0 + qs) & 7) + 8 * pos;
-          if (nl >= total) {
+          const long long cand = ((x0 + qs) & 7) + 8LL * pos;
+          nl = (int)cand;
+          if (cand < 0 || cand >= total) {
             ++qs;
             nl = fetch_now();
           }
