@@ -107,6 +107,8 @@ def test_fwd_scale_edge_cases(scale):
 # lengths, both head dims, GQA and Nq != Nk exercise its tiling and masks.
 LONG_CASES = [
     (1, 2, 1, 4097, 4097, 128, True),
+    (1, 1, 1, 8300, 8300, 128, True),   # 8-wavefront causal kernel, ragged last Q tile
+    (1, 2, 2, 4500, 4500, 128, False),  # two-group kernel, ragged
     (1, 2, 2, 4100, 4100, 64, True),
     (1, 2, 1, 333, 4200, 128, False),
     (1, 1, 1, 4096, 4096, 64, False),
