@@ -6,6 +6,7 @@ CPU-baseline leg of the benchmark, never by the library itself.
 
 from .attention import (  # noqa: F401
     backward,
+    backward_dq_rows,
     backward_head,
     backward_varlen,
     forward,

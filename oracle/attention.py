@@ -152,6 +152,29 @@ def backward_head(qh, kh, vh, doh, scale, causal, row_block=256):
     return dQ, dK, dV
 
 
+def backward_dq_rows(qh, kh, vh, doh, scale, causal, rows, row_block=64):
+    """dQ for the query rows ``rows`` of one head (page 6.2, section 7; CSDN
+    article, 3.1.2): every quantity of row i is local to that row, so
+    P_i = exp(S_i - L_i), O_i = P_i V, D_i = dO_i . O_i, dP_i = dO_i V^T,
+    dS_i = P_i o (dP_i - D_i) and dQ_i = s dS_i K need only row i of Q and dO
+    and all of K and V. Returns dQ [n, d] in float64 (for long sequences,
+    where the full backward is out of reach)."""
+    qh, kh, vh, doh = _as64(qh), _as64(kh), _as64(vh), _as64(doh)
+    s = float(scale)
+    idx = np.asarray(rows, dtype=np.int64)
+    dQ = np.empty((idx.size, qh.shape[1]))
+    for a in range(0, idx.size, row_block):
+        r = idx[a:a + row_block]
+        S = _scores(qh[r], r, kh, s, causal)
+        m = S.max(axis=1)
+        Lb = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+        P = np.exp(S - Lb[:, None])
+        D = row_dot(doh[r], P @ vh)
+        dS = P * (doh[r] @ vh.T - D[:, None])
+        dQ[a:a + r.size] = s * (dS @ kh)
+    return dQ
+
+
 def backward(q, k, v, do, scale, causal):
     """Exact attention gradients for upstream gradient dO.
 
