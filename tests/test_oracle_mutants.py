@@ -27,8 +27,13 @@ MUTANTS = {
     "dk_operand_swapped": ("dK += s * (dS.T @ qh[r])", "dK += s * (dS.T @ doh[r])"),
     "gqa_interleaved_groups": ("g = h // G\n            O[b, h]", "g = h % Hkv\n            O[b, h]"),
     "gqa_backward_not_summed": ("dK[b, g] += dk", "dK[b, g] = dk"),
-    "p_recompute_unmasked_in_backward": ("S = _scores(qh[r], r, kh, s, causal)\n        m = S.max(axis=1)\n        Lb = m + np.log(np.exp",
-                                         "S = _scores(qh[r], r, kh, s, False)\n        m = S.max(axis=1)\n        Lb = m + np.log(np.exp"),
+    # the full backward's recompute (the row-local dQ has its own pin against it)
+    "p_recompute_unmasked_in_backward": ("S = _scores(qh[r], r, kh, s, causal)\n        m = S.max(axis=1)\n"
+                                         "        Lb = m + np.log(np.exp(S - m[:, None]).sum(axis=1))\n"
+                                         "        P = np.exp(S - Lb[:, None])\n        Ob = P @ vh",
+                                         "S = _scores(qh[r], r, kh, s, False)\n        m = S.max(axis=1)\n"
+                                         "        Lb = m + np.log(np.exp(S - m[:, None]).sum(axis=1))\n"
+                                         "        P = np.exp(S - Lb[:, None])\n        Ob = P @ vh"),
 }
 
 
