@@ -129,8 +129,55 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_wave_bas
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_wave_base, 16, 0, 0);
 }
 
+// The same pointer, read from the first active lane into scalar registers
+// (the caller guarantees it is wave-uniform). The result is opaque to the
+// compiler's loop analysis, so address arithmetic on it is not hoisted into
+// per-lane registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t x = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// Word 3 of a raw buffer resource for gfx9-family GPUs (gfx950 included):
+// 32-bit data format, no swizzle; with stride 0 the resource is a plain
+// byte-addressed range of num_records bytes.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// HBM -> LDS through a buffer resource (buffer_load_dwordx4 ... lds): lane l
+// fetches the 16 bytes at byte voff of the resource into
+// lds_wave_base + 16*l. lds_wave_base must be uniform across the wavefront.
+__device__ __forceinline__ void load_lds_16_buf(__amdgpu_buffer_rsrc_t rs, int voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
 // Wait until this wavefront's outstanding vector-memory loads (including the
 // HBM -> LDS ones) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until this wavefront's LDS instructions have completed:
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maximum, no wait).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that orders the compiler's memory accesses around it but
+// adds no waits of its own (s_barrier between two compiler memory fences).
+// The caller waits for what the other wavefronts must see first: its own
+// HBM -> LDS loads (wait_vmem_n) and, before others may overwrite LDS it has
+// read, its LDS reads (wait_lds).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wavefront's vector-memory loads are still in
+// flight (s_waitcnt vmcnt(N); the counter is 6 bits, split over simm16 bits
+// 3:0 and 15:14). Loads retire from the counter in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 }  // namespace fa

@@ -64,12 +64,20 @@ fwd_kernel(FwdArgs a) {
   constexpr int BR = T::BR, BC = T::BC, NKB = T::NKB, ROWB = T::ROWB, RC = T::RC, TILEB = T::TILEB;
   constexpr int CPW = T::CPW;
 
-  // Two K/V buffers as separate objects so that the compiler can tell that
-  // the prefetch into one never aliases the reads of the other.
+  // The d = 128 bf16 one-item-per-workgroup instances keep three K buffers
+  // and two V buffers (80 KiB, so two 4-wavefront workgroups still share a
+  // CU): K_j is fetched two steps before its scores, V_j one step before its
+  // product (measured 1-6 % faster than two of each at d = 128; at d = 64,
+  // where one more tile per Q tile takes the masked body, 2-8 % slower on
+  // sequences up to 4K). The other instances keep two of each. Every buffer
+  // is a separate object so that the compiler can tell that the prefetch
+  // into one never aliases the reads of another.
+  constexpr bool DEEP = !F32IN && !PERSIST && D == 128;
   __shared__ __attribute__((aligned(16))) char sK0[TILEB];
   __shared__ __attribute__((aligned(16))) char sV0[TILEB];
   __shared__ __attribute__((aligned(16))) char sK1[TILEB];
   __shared__ __attribute__((aligned(16))) char sV1[TILEB];
+  __shared__ __attribute__((aligned(16))) char sK2[DEEP ? TILEB : 16];
 
   const int tid = threadIdx.x;
   int lane = tid & 63;  // lane, g, l32 are only changed by the persistent loop's empty asm
@@ -124,8 +132,9 @@ fwd_kernel(FwdArgs a) {
       qhead = (size_t)(b * a.Hq + hq) * a.Nq;
       kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
     }
-    const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
-    const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
+    // (in scalar registers for the three-buffer loop's scalar-base loads)
+    const char* __restrict__ Kh = DEEP ? uniform_ptr((const char*)a.k + kvhead * ROWB) : (const char*)a.k + kvhead * ROWB;
+    const char* __restrict__ Vh = DEEP ? uniform_ptr((const char*)a.v + kvhead * ROWB) : (const char*)a.v + kvhead * ROWB;
 
     // ---- Q fragments (B operand of S^T = K Q^T), loaded once ----------------
     using QFrag = std::conditional_t<F32IN, float, bf16x8>;
@@ -196,6 +205,33 @@ fwd_kernel(FwdArgs a) {
       }
     };
 
+    // One tile (K or V, from head base Xh) into Xt. Each load is the tile's
+    // scalar base plus the lane's 32-bit offset (global_load_lds_dwordx4 with
+    // a scalar address): the tile base is made opaque, and so is the offset
+    // right before its use, so that neither is folded into per-lane 64-bit
+    // pointers kept live across the loop. In a tile that runs past the end of
+    // K/V, rows past the end read the last row instead (their scores are
+    // masked).
+    auto issue_one = [&](int jt, const char* __restrict__ Xh, char* Xt) __attribute__((always_inline)) {
+      const int kv0 = jt * BC;
+      const char* Xb = uniform_ptr(Xh + (size_t)kv0 * ROWB);
+      unsigned o[CPW];
+  #pragma unroll
+      for (int u = 0; u < CPW; ++u) o[u] = (unsigned)(ldoff[u % NP] + (u / NP) * NP * RPL * ROWB);
+      if (kv0 + BC > Nk) {
+        const unsigned last = (unsigned)(Nk - 1 - kv0);  // last row of K/V in this tile
+  #pragma unroll
+        for (int u = 0; u < CPW; ++u)
+          if (o[u] / ROWB > last) o[u] = last * ROWB + o[u] % ROWB;
+      }
+  #pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        unsigned ou = o[u];
+        asm volatile("" : "+v"(ou));
+        load_lds_16(Xb + ou, Xt + (wu * CPW + u) * 64 * 16);
+      }
+    };
+
     f32x16 oacc[D / 32];
   #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -221,11 +257,11 @@ fwd_kernel(FwdArgs a) {
           voff[db][h] = tile_off<RC>(4 * g + 8 * h + (j >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2);
     }
 
-    auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
+    // Scores, mask and online softmax of tile jt: on return sacc holds P.
+    auto body_s = [&](auto mask_tag, int jt, const char* Kt, f32x16(&sacc)[NKB]) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int kv0 = jt * BC;
       // ---- S^T = K_j Q_i^T ------------------------------------------------------
-      f32x16 sacc[NKB];
   #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         sacc[kb] = f32x16{};
@@ -283,8 +319,10 @@ fwd_kernel(FwdArgs a) {
           rs += p;
         }
       lsum += rs;
+    };
 
-      // ---- O^T += V_j^T P^T ---------------------------------------------------------
+    // O^T += V_j^T P^T for the probabilities in sacc.
+    auto body_pv = [&](const char* Vt, f32x16(&sacc)[NKB]) __attribute__((always_inline)) {
       if constexpr (F32IN) {
   #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -319,6 +357,12 @@ fwd_kernel(FwdArgs a) {
       }
     };
 
+    auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
+      f32x16 sacc[NKB];
+      body_s(mask_tag, jt, Kt, sacc);
+      body_pv(Vt, sacc);
+    };
+
     // A step computes tile jt from (Kt, Vt) while tile jt+1 streams into
     // (Kn, Vn). A wavefront whose 32 rows all lie above the tile skips it;
     // tiles that cross the diagonal or the end of K/V take the masked body.
@@ -349,20 +393,101 @@ fwd_kernel(FwdArgs a) {
     // loop runs the unmasked body only. The last BR / BC tiles take the
     // generic step.
     constexpr int NTAIL = BR / BC;
-    const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
-    issue_tile(0, sK0, sV0);
-    wait_vmem();
-    __syncthreads();
-    int jt = 0;
-    for (; jt + 1 < n_main; jt += 2) {
-      step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
-      step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
-    }
-    for (; jt < n_kv; ++jt) {
-      if (jt & 1)
-        step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
-      else
-        step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+    if constexpr (DEEP) {
+      // Loads are issued in the order K_0, V_0, K_1 (here), then V_{j+1},
+      // K_{j+2} at the top of step j, into K buffer j % 3 and V buffer j % 2.
+      // Step j ends by waiting for K_{j+1} and V_{j+1}: the vector-memory
+      // counter retires loads in issue order, so that is "at most the loads
+      // of K_{j+2} in flight". The barrier after it makes every wavefront's
+      // share of both tiles visible; it also follows the completion of all
+      // of the wavefront's LDS reads, so the loads of step j+1 may overwrite
+      // V_j and K_j. The barrier is a plain s_barrier between compiler memory
+      // fences: a workgroup fence would make the compiler wait for every load
+      // in flight. Steps before n_fast are unmasked for every wavefront and
+      // have both loads to issue; the others (the last few tiles of a Q
+      // tile) check everything and take the masked body.
+      const int n_fast = max(0, min(n_kv - NTAIL, n_kv - 2));
+      auto dstep = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Vn, char* Kn2)
+                       __attribute__((always_inline)) {
+        constexpr bool GENERIC = decltype(generic_tag)::value;
+        const bool has1 = !GENERIC || jt + 1 < n_kv;
+        const bool has2 = !GENERIC || jt + 2 < n_kv;
+        if (has1) issue_one(jt + 1, Vh, Vn);
+        if (has2) issue_one(jt + 2, Kh, Kn2);
+        f32x16 sacc[NKB];
+        if constexpr (GENERIC) {
+          if (!CAUSAL || jt * BC <= q0w + 31) {
+            body_s(std::true_type{}, jt, Kt, sacc);
+            body_pv(Vt, sacc);
+          }
+          if (has2)
+            wait_vmem_n<CPW>();
+          else
+            wait_vmem_n<0>();
+        } else {
+          body_s(std::false_type{}, jt, Kt, sacc);
+          body_pv(Vt, sacc);
+          wait_vmem_n<CPW>();
+        }
+        wait_lds();
+        lds_barrier();
+      };
+      issue_one(0, Kh, sK0);
+      issue_one(0, Vh, sV0);
+      if (n_kv > 1) {
+        issue_one(1, Kh, sK1);
+        wait_vmem_n<CPW>();
+      } else {
+        wait_vmem_n<0>();
+      }
+      __syncthreads();
+      // Main loop: unmasked steps only, unrolled over the six (K buffer,
+      // V buffer) phases so that every buffer is a compile-time choice; it
+      // can leave after any phase.
+      int jt = 0;
+      if (n_fast > 0) {
+        while (true) {
+          dstep(std::false_type{}, jt, sK0, sV0, sV1, sK2);
+          if (++jt >= n_fast) break;
+          dstep(std::false_type{}, jt, sK1, sV1, sV0, sK0);
+          if (++jt >= n_fast) break;
+          dstep(std::false_type{}, jt, sK2, sV0, sV1, sK1);
+          if (++jt >= n_fast) break;
+          dstep(std::false_type{}, jt, sK0, sV1, sV0, sK2);
+          if (++jt >= n_fast) break;
+          dstep(std::false_type{}, jt, sK1, sV0, sV1, sK0);
+          if (++jt >= n_fast) break;
+          dstep(std::false_type{}, jt, sK2, sV1, sV0, sK1);
+          if (++jt >= n_fast) break;
+        }
+      }
+      // The last few tiles: generic steps, in the phase the main loop left.
+      for (; jt < n_kv; ++jt) {
+        switch (jt % 6) {
+          case 0: dstep(std::true_type{}, jt, sK0, sV0, sV1, sK2); break;
+          case 1: dstep(std::true_type{}, jt, sK1, sV1, sV0, sK0); break;
+          case 2: dstep(std::true_type{}, jt, sK2, sV0, sV1, sK1); break;
+          case 3: dstep(std::true_type{}, jt, sK0, sV1, sV0, sK2); break;
+          case 4: dstep(std::true_type{}, jt, sK1, sV0, sV1, sK0); break;
+          default: dstep(std::true_type{}, jt, sK2, sV1, sV0, sK1); break;
+        }
+      }
+    } else {
+      const int n_main = n_kv > NTAIL ? n_kv - NTAIL : 0;
+      issue_tile(0, sK0, sV0);
+      wait_vmem();
+      __syncthreads();
+      int jt = 0;
+      for (; jt + 1 < n_main; jt += 2) {
+        step(std::false_type{}, jt, sK0, sV0, sK1, sV1);
+        step(std::false_type{}, jt + 1, sK1, sV1, sK0, sV0);
+      }
+      for (; jt < n_kv; ++jt) {
+        if (jt & 1)
+          step(std::true_type{}, jt, sK1, sV1, sK0, sV0);
+        else
+          step(std::true_type{}, jt, sK0, sV0, sK1, sV1);
+      }
     }
 
     // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
