@@ -430,13 +430,9 @@ struct DkdvTile {
   static constexpr int ROWB = D * 2, RC = ROWB / 16;
   static constexpr int QTILEB = BQ * ROWB;
   static constexpr int QCPW = QTILEB / (1024 * NW);
-  static constexpr int XB = 4 * 64 * 16;              // per wavefront: P and dS, 2 x bf16x8 each per lane
-  static constexpr int OFF_X = 0;                     // [NW][XB]
-  static constexpr int OFF_Q = OFF_X + NW * XB;       // [2][QTILEB]
-  static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;   // [2][QTILEB]
-  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;   // [2][BQ]
-  static constexpr int OFF_D = OFF_L + 2 * BQ * 4;    // [2][BQ]
-  static constexpr int LDS_BYTES = OFF_D + 2 * BQ * 4;
+  static constexpr int XB = 4 * 64 * 16;  // per wavefront: P and dS, 2 x bf16x8 each per lane
+  // LDS (static): exchange [NW][XB], Q and dO tiles x 2, L and D x 2
+  static constexpr int LDS_BYTES = NW * XB + 4 * QTILEB + 4 * BQ * 4;
   static_assert(QTILEB % (1024 * NW) == 0, "tiles must split evenly");
   static_assert(D % 64 == 0, "each wavefront takes whole 32-wide head-dim blocks of one half");
 };
@@ -448,12 +444,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int QCPW = T::QCPW, XB = T::XB;
   constexpr int NKK = D / 16, NDH = D / 64;  // NDH: 32-wide head-dim blocks per half
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* const sX = smem + T::OFF_X;
-  char* const sQ = smem + T::OFF_Q;
-  char* const sDO = smem + T::OFF_DO;
-  float* const sL = (float*)(smem + T::OFF_L);
-  float* const sD = (float*)(smem + T::OFF_D);
+  // Static LDS, one object per buffer: with the loop unrolled over the two
+  // Q/dO buffers every LDS access names its buffer at compile time, so the
+  // compiler can tell that the reads of one buffer never alias the HBM->LDS
+  // loads in flight into the other and does not wait for them.
+  __shared__ __attribute__((aligned(16))) char sX[T::NW * XB];
+  __shared__ __attribute__((aligned(16))) char sQ0[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sQ1[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sDO0[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sDO1[QTILEB];
+  __shared__ __attribute__((aligned(16))) float sL0[BQ];
+  __shared__ __attribute__((aligned(16))) float sL1[BQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BQ];
+  __shared__ __attribute__((aligned(16))) float sD1[BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -538,41 +541,52 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float c = a.c;
   const float scale = a.scale;
 
+  // The next Q block's L and D are loaded into registers as its Q/dO tiles
+  // are issued and only used (scaled, masked, stored to LDS) at the end of
+  // the current block: using them at once would make the wavefront wait for
+  // every load in flight, the tiles just issued included.
   float lr = 0.0f, dr = 0.0f;
-  auto issue_q = [&](int it, int buf) __attribute__((always_inline)) {
+  bool lok = false;
+  auto issue_q = [&](int it, char* nQ, char* nDO) __attribute__((always_inline)) {
     const int hm = it / n_i;
     const int i = i_first + it % n_i;
     const int hq = hkv * a.G + hm;
     const size_t qhead = q_base(hq);
     const int q0 = i * BQ;
-    const char* Qh = (const char*)a.q + qhead * ROWB;
-    const char* Oh = (const char*)a.dout + qhead * ROWB;
+    if (tid < BQ) {
+      lok = q0 + tid < Nq;
+      const size_t r = qhead + q0 + (lok ? tid : 0);  // row q0 < Nq exists
+      lr = a.lse[r];
+      dr = a.dvec[r];
+    }
+    // Scalar tile base plus a 32-bit per-lane offset (rows past the end of
+    // Q read the last row); both are kept opaque so that the loads stay in
+    // the scalar-address form.
+    const char* Qb = uniform_ptr((const char*)a.q + (qhead + q0) * ROWB);
+    const char* Ob = uniform_ptr((const char*)a.dout + (qhead + q0) * ROWB);
+    const int last = Nq - 1 - q0;
 #pragma unroll
     for (int u = 0; u < QCPW; ++u) {
       const int cb = (w * QCPW + u) * 64;
       const int idx = cb + lane;
       const int row = idx / RC, pc = idx % RC;
       const int lc = pc ^ swz<RC>(row);
-      const size_t off = (size_t)min(q0 + row, Nq - 1) * ROWB + lc * 16;
-      load_lds_16(Qh + off, sQ + buf * QTILEB + cb * 16);
-      load_lds_16(Oh + off, sDO + buf * QTILEB + cb * 16);
-    }
-    if (tid < BQ) {
-      const bool ok = q0 + tid < Nq;
-      lr = ok ? a.lse[qhead + q0 + tid] * kLog2e : INFINITY;
-      dr = ok ? a.dvec[qhead + q0 + tid] : 0.0f;
+      unsigned off = (unsigned)(min(row, last) * ROWB + lc * 16);
+      asm volatile("" : "+v"(off));
+      load_lds_16(Qb + off, nQ + cb * 16);
+      load_lds_16(Ob + off, nDO + cb * 16);
     }
   };
-  auto store_ld = [&](int buf) __attribute__((always_inline)) {
+  auto store_ld = [&](float* nL, float* nD) __attribute__((always_inline)) {
     if (tid < BQ) {
-      sL[buf * BQ + tid] = lr;
-      sD[buf * BQ + tid] = dr;
+      nL[tid] = lok ? lr * kLog2e : INFINITY;
+      nD[tid] = lok ? dr : 0.0f;
     }
   };
 
   if (total > 0) {
-    issue_q(0, 0);
-    store_ld(0);
+    issue_q(0, sQ0, sDO0);
+    store_ld(sL0, sD0);
   }
   wait_vmem();
   __syncthreads();
@@ -653,16 +667,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
   };
 
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
+  // One Q block: its tiles in (tQ, tDO, tL, tD), the next block's loads go to
+  // (nQ, nDO, nL, nD).
+  auto block = [&](int it, const char* tQ, const char* tDO, const float* tL, const float* tD, char* nQ, char* nDO,
+                   float* nL, float* nD) __attribute__((always_inline)) {
     const int i = i_first + it % n_i;
     const int q0 = i * BQ;
     const bool has_next = it + 1 < total;
-    if (has_next) issue_q(it + 1, buf ^ 1);
-    const char* tQ = sQ + buf * QTILEB;
-    const char* tDO = sDO + buf * QTILEB;
-    const float* tL = sL + buf * BQ;
-    const float* tD = sD + buf * BQ;
+    if (has_next) issue_q(it + 1, nQ, nDO);
     // A (key group, query half) block is skipped when all its keys lie after
     // all its queries.
     const bool act0 = !CAUSAL || kv0 + 32 * kg <= q0 + 31;
@@ -680,7 +692,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       *(bf16x8*)(myX + (2 * 64 + lane) * 16) = dsb[0];
       *(bf16x8*)(myX + (3 * 64 + lane) * 16) = dsb[1];
     }
-    __syncthreads();
+    // The exchange needs only the P/dS writes to have landed; the Q/dO tiles
+    // of the next block stay in flight across this barrier.
+    wait_lds();
+    lds_barrier();
     if (mine) grads(h, tQ, tDO, pb, dsb);
     if (h ? act0 : act1) {
       bf16x8 ppb[2], pds[2];
@@ -690,9 +705,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       pds[1] = *(const bf16x8*)(ptX + (3 * 64 + lane) * 16);
       grads(h ^ 1, tQ, tDO, ppb, pds);
     }
-    if (has_next) store_ld(buf ^ 1);
+    if (has_next) store_ld(nL, nD);
     wait_vmem();
     __syncthreads();
+  };
+  for (int it = 0; it < total; it += 2) {
+    block(it, sQ0, sDO0, sL0, sD0, sQ1, sDO1, sL1, sD1);
+    if (it + 1 >= total) break;
+    block(it + 1, sQ1, sDO1, sL1, sD1, sQ0, sDO0, sL0, sD0);
   }
 
   // ---- epilogue: dK = scale * dK^T, dV = dV^T for this head-dim half --------
@@ -985,10 +1005,8 @@ template <int D, bool CAUSAL, bool GF32>
 static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   using T = DkdvTile<D>;
   auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-  if (e != hipSuccess) return e;
   const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), T::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1044,12 +1062,10 @@ static hipError_t launch_bwd_varlen_t(const BwdArgs& a, bool o_f32, hipStream_t 
   {
     using T = DkdvTile<D>;
     auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS_BYTES);
-    if (e != hipSuccess) return e;
     const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
     if (blocks > 0) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), T::LDS_BYTES, s, a);
-      e = hipGetLastError();
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, s, a);
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
