@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
                    help="summarise rocprofv3 output under DIR/{trace,fetch,write} (no GPU needed) and record "
                         "the HBM bytes per launch for the current kernel sources")
+    p.add_argument("--summarize-pmc", default=None, metavar="DIR",
+                   help="summarise a rocprofv3 --pmc run of SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+                        "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE under DIR (no GPU needed)")
     p.add_argument("--calibration-mib", type=int, default=256, help="copy size used by the counter runs")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, copy a MIB-MiB buffer 3 times (a plain copy kernel of known size, to "
@@ -486,6 +489,45 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
     print(f"\nkernel sources sha256 {rec['kernel_sources_sha256']}")
 
 
+def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024):
+    """Per-kernel averages of one rocprofv3 --pmc run: clock (GRBM_GUI_ACTIVE,
+    summed over the n_xcd XCD instances, over the dispatch's duration), MFMA
+    utilisation (SQ_VALU_MFMA_BUSY_CYCLES over n_simd SIMDs x the kernel's
+    cycles, the rocprofv3 MfmaUtil expression), instructions per wavefront,
+    and LDS bank-conflict cycles."""
+    import collections
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(prof_dir, "*counter_collection.csv"))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {prof_dir}")
+    disp = collections.defaultdict(lambda: collections.defaultdict(dict))
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            d = disp[r["Kernel_Name"]][r["Dispatch_Id"]]
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    print("| kernel | entry point | dispatches | µs | clock GHz | MFMA busy % | VALU instr / wave | "
+          "MFMA instr / wave | VALU / MFMA | LDS instr / wave | LDS bank-conflict cycles |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, ds in disp.items():
+        call = _call_of(name)
+        if call is None:
+            continue
+        n = len(ds)
+        avg = {k: sum(d.get(k, 0.0) for d in ds.values()) / n
+               for k in ("_ns", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU",
+                         "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")}
+        cyc = avg["GRBM_GUI_ACTIVE"] / n_xcd
+        waves = max(avg["SQ_WAVES"], 1.0)
+        mfma_busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd) if cyc else 0.0
+        v_per_m = avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"] if avg["SQ_INSTS_MFMA"] else float("nan")
+        print(f"| `{name}` | {call} | {n} | {avg['_ns'] / 1e3:.1f} | {cyc / avg['_ns']:.2f} | {mfma_busy:.1f} | "
+              f"{avg['SQ_INSTS_VALU'] / waves:.0f} | {avg['SQ_INSTS_MFMA'] / waves:.0f} | {v_per_m:.2f} | "
+              f"{avg['SQ_INSTS_LDS'] / waves:.0f} | {avg['SQ_LDS_BANK_CONFLICT']:.0f} |")
+
+
 def measured_traffic(call):
     """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
@@ -527,6 +569,8 @@ def main():
     args = parse()
     if args.summarize_profiles:
         return summarize_profiles(args.summarize_profiles, args.calibration_mib)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the attention path runs on one GPU)", file=sys.stderr)

@@ -212,13 +212,15 @@ fwd_kernel(FwdArgs a) {
     // pointers kept live across the loop. In a tile that runs past the end of
     // K/V, rows past the end read the last row instead (their scores are
     // masked).
-    auto issue_one = [&](int jt, const char* __restrict__ Xh, char* Xt) __attribute__((always_inline)) {
+    // FULL: the caller knows that the tile lies inside K/V.
+    auto issue_one = [&](auto full_tag, int jt, const char* __restrict__ Xh, char* Xt) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
       const int kv0 = jt * BC;
       const char* Xb = uniform_ptr(Xh + (size_t)kv0 * ROWB);
       unsigned o[CPW];
   #pragma unroll
       for (int u = 0; u < CPW; ++u) o[u] = (unsigned)(ldoff[u % NP] + (u / NP) * NP * RPL * ROWB);
-      if (kv0 + BC > Nk) {
+      if (!FULL && kv0 + BC > Nk) {
         const unsigned last = (unsigned)(Nk - 1 - kv0);  // last row of K/V in this tile
   #pragma unroll
         for (int u = 0; u < CPW; ++u)
@@ -406,14 +408,15 @@ fwd_kernel(FwdArgs a) {
       // in flight. Steps before n_fast are unmasked for every wavefront and
       // have both loads to issue; the others (the last few tiles of a Q
       // tile) check everything and take the masked body.
-      const int n_fast = max(0, min(n_kv - NTAIL, n_kv - 2));
+      // (n_fast also keeps tile j + 2 of a fast step inside K/V)
+      const int n_fast = max(0, min(min(n_kv - NTAIL, n_kv - 2), Nk / BC - 2));
       auto dstep = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Vn, char* Kn2)
                        __attribute__((always_inline)) {
         constexpr bool GENERIC = decltype(generic_tag)::value;
         const bool has1 = !GENERIC || jt + 1 < n_kv;
         const bool has2 = !GENERIC || jt + 2 < n_kv;
-        if (has1) issue_one(jt + 1, Vh, Vn);
-        if (has2) issue_one(jt + 2, Kh, Kn2);
+        if (has1) issue_one(std::bool_constant<!GENERIC>{}, jt + 1, Vh, Vn);
+        if (has2) issue_one(std::bool_constant<!GENERIC>{}, jt + 2, Kh, Kn2);
         f32x16 sacc[NKB];
         if constexpr (GENERIC) {
           if (!CAUSAL || jt * BC <= q0w + 31) {
@@ -432,10 +435,10 @@ fwd_kernel(FwdArgs a) {
         wait_lds();
         lds_barrier();
       };
-      issue_one(0, Kh, sK0);
-      issue_one(0, Vh, sV0);
+      issue_one(std::false_type{}, 0, Kh, sK0);
+      issue_one(std::false_type{}, 0, Vh, sV0);
       if (n_kv > 1) {
-        issue_one(1, Kh, sK1);
+        issue_one(std::false_type{}, 1, Kh, sK1);
         wait_vmem_n<CPW>();
       } else {
         wait_vmem_n<0>();
