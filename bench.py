@@ -367,7 +367,7 @@ def csrc_sha256():
 # or mangled for the preprocess kernel, whose last template argument says
 # whether it also zeroes dQ: only fa_bwd_atomic's does).
 CALL_KERNELS = {
-    "fa_fwd": ("void fa::fwd_kernel<", "void fa::fwd_pp_kernel<"),
+    "fa_fwd": ("void fa::fwd_kernel<",),
     "fa_bwd": ("void fa::bwd_dkdv_kernel<", "void fa::bwd_dq_kernel<"),
     "fa_bwd_atomic": ("void fa::bwd_kernel<",),
     "fa_quantize_fp8": ("void fa::quantize_fp8_kernel<",),

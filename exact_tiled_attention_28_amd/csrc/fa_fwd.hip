@@ -580,291 +580,15 @@ fwd_kernel(FwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 forward with two wavefront groups in opposite phases
-// ---------------------------------------------------------------------------
-//
-// The non-matmul work (mask, max, exp, sum, rescale) costs about as much
-// issue time as the two products of a tile, and a wavefront cannot issue its
-// own softmax while its MFMAs wait on each other. The FlashAttention-3 news
-// page ("pingpong scheduling giữa các warpgroup") overlaps the softmax of
-// one warpgroup with the GEMMs of another; here the same idea is laid out for
-// a CDNA4 compute unit: one workgroup of 8 wavefronts (2 per SIMD) owns a
-// 256-row Q tile; wavefronts 0-3 (group A) and 4-7 (group B) each own 32
-// rows and alternate between
-//   a matrix phase:  S_j = K_j Q^T and O^T += V_{j-1}^T P_{j-1}^T (MFMA), and
-//   a softmax phase: P_j = online softmax of S_j, rescale of O (VALU),
-// with group B one phase behind group A, so on every SIMD one wavefront is in
-// its matrix phase while the other is in its softmax phase. Phases end at
-// workgroup barriers. K_j is read in phases 2j (A) and 2j+1 (B), V_j in
-// phases 2j+2 (A) and 2j+3 (B); each is fetched two phases ahead into a
-// double buffer (HBM -> LDS, no registers).
-template <int D, bool CAUSAL, bool OUTF32>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_pp_kernel(FwdArgs a) {
-  constexpr int NW = 8, BR = 32 * NW, BC = 64, NKB = BC / 32;
-  constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB;
-  constexpr int CPW = TILEB / (1024 * NW);
-  constexpr int NQF = D / 16;
-  static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole wave loads");
-
-  __shared__ __attribute__((aligned(16))) char sK0[TILEB];
-  __shared__ __attribute__((aligned(16))) char sV0[TILEB];
-  __shared__ __attribute__((aligned(16))) char sK1[TILEB];
-  __shared__ __attribute__((aligned(16))) char sV1[TILEB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int grp = w >> 2;  // 0: group A, 1: group B (one phase behind)
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-
-  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
-  const int b = ui.unit / a.Hkv;
-  const int hkv = ui.unit % a.Hkv;
-  const int rank = ui.item / a.G;
-  const int hq = hkv * a.G + ui.item % a.G;
-  const int qt = CAUSAL ? (a.n_q_tiles - 1 - rank) : rank;
-  const int q0 = qt * BR;
-  const int q0w = q0 + 32 * w;
-  const int qrow = q0w + l32;
-
-  const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
-  const size_t kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
-  const char* __restrict__ Kh = (const char*)a.k + kvhead * ROWB;
-  const char* __restrict__ Vh = (const char*)a.v + kvhead * ROWB;
-
-  bf16x8 qf[NQF];
-  {
-    const char* Qr = (const char*)a.q + (qhead + qrow) * ROWB;
-    const unsigned sign = a.neg ? 0x80008000u : 0u;
-#pragma unroll
-    for (int kk = 0; kk < NQF; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < a.Nq) x = *(const u32x4*)(Qr + (kk * 16 + 8 * g) * 2);
-      x ^= sign;
-      qf[kk] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  const int kv_end = kv_end_for(q0, BR, a.Nk, CAUSAL);
-  const int n_kv = ceil_div(kv_end, BC);
-  // Tiles this wavefront computes (causal rows q0w..q0w+31 need keys up to
-  // q0w+31 only).
-  const int n_w = CAUSAL ? min(n_kv, ceil_div(min(kv_end, q0w + 32), BC)) : n_kv;
-
-  auto issue = [&](const char* src, int jt, char* dst) __attribute__((always_inline)) {
-    const int kv0 = jt * BC;
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int cb = (w * CPW + u) * 64;
-      const int idx = cb + lane;
-      const int row = idx / RC, pc = idx % RC;
-      const int lc = pc ^ swz<RC>(row);
-      const int grow = min(kv0 + row, a.Nk - 1);
-      load_lds_16(src + (size_t)grow * ROWB + lc * 16, dst + cb * 16);
-    }
-  };
-
-  int koff[NQF];
-#pragma unroll
-  for (int kk = 0; kk < NQF; ++kk) koff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
-  int voff[D / 32][2];
-  {
-    const int j = lane & 15;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        voff[db][h] = tile_off<RC>(4 * g + 8 * h + (j >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2);
-  }
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  f32x16 sacc[NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-  bf16x8 pb[BC / 16];
-#pragma unroll
-  for (int t = 0; t < BC / 16; ++t) pb[t] = bf16x8{};
-  float m = -INFINITY;  // running max, log2 units (scaled scores)
-  float lsum = 0.0f;    // running sum over this half-wave's keys
-  const float c = a.c;
-
-  // matrix phase: S_j = K_j Q^T (if j < n_w) and O^T += V_{j-1}^T P_{j-1}^T
-  auto matrix_phase = [&](int j, const char* Kt, const char* Vp) __attribute__((always_inline)) {
-    if (j >= 1 && j - 1 < n_w) {
-#pragma unroll
-      for (int t = 0; t < BC / 16; ++t)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const char* vp = Vp + 16 * t * ROWB;
-          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][0]));
-          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(vp + voff[db][1]));
-          oacc[db] = mfma_bf16(cat4(lo, hi), pb[t], oacc[db]);
-        }
-    }
-    if (j < n_w) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NQF; ++kk)
-          acc = mfma_bf16(*(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB), qf[kk], acc);
-        sacc[kb] = acc;
-      }
-    }
-  };
-
-  // softmax phase for tile j: mask (diagonal / ragged tiles), online max,
-  // rescale of O when a row max grew, P_j = exp2(S c - m) packed to bf16.
-  auto softmax_body = [&](auto mask_tag, int j) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int kv0 = j * BC;
-    if constexpr (MASK) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < a.Nk && (!CAUSAL || key <= qrow);
-          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    const float mxs = half_swap_max(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mxs > m) != 0) {
-      const float m_new = fmaxf(m, mxs);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-    }
-    float rs = 0.0f;
-#pragma unroll
-    for (int t = 0; t < BC / 16; ++t) {
-      float pv[8];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const float sv = sacc[t >> 1][8 * (t & 1) + v];
-        float p = fast_exp2(fmaf(sv, c, -m));
-        if constexpr (MASK) p = (sv == -INFINITY) ? 0.0f : p;
-        pv[v] = p;
-        rs += p;
-      }
-      pb[t] = to_bf16x8(pv);
-    }
-    lsum += rs;
-  };
-  auto softmax_phase = [&](int j) __attribute__((always_inline)) {
-    if (j >= n_w) return;
-    const int kv0 = j * BC;
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > a.Nk);
-    if (need_mask)
-      softmax_body(std::true_type{}, j);
-    else
-      softmax_body(std::false_type{}, j);
-  };
-
-  issue(Kh, 0, sK0);
-  wait_vmem();
-  __syncthreads();
-
-  // Phase p: group A works on step p, group B on step p - 1; step 2j is the
-  // matrix phase of tile j (K_j from buffer j%2, V_{j-1} from buffer
-  // (j-1)%2), step 2j+1 its softmax phase; step 2*n_kv is the last P V
-  // product. At even phases 2j the loads of K_{j+1} and V_j are issued; they
-  // are waited for at the end of phase 2j+1. The loop is unrolled by 4 so
-  // that every buffer is a compile-time choice.
-  const int n_phases = 2 * n_kv + 2;
-  auto phase = [&](int p, auto p4_tag) __attribute__((always_inline)) {
-    constexpr int P4 = decltype(p4_tag)::value;
-    if constexpr (P4 == 0 || P4 == 2) {
-      const int j = p >> 1;
-      if (j + 1 < n_kv) issue(Kh, j + 1, P4 == 0 ? sK1 : sK0);
-      if (j < n_kv) issue(Vh, j, P4 == 0 ? sV0 : sV1);
-    }
-    const int st = p - grp;
-    if (st >= 0) {
-      const int j = st >> 1;
-      if (grp == 0) {
-        if constexpr (P4 == 0) matrix_phase(j, sK0, sV1);
-        if constexpr (P4 == 2) matrix_phase(j, sK1, sV0);
-        if constexpr (P4 & 1) softmax_phase(j);
-      } else {
-        if constexpr (P4 == 1) matrix_phase(j, sK0, sV1);
-        if constexpr (P4 == 3) matrix_phase(j, sK1, sV0);
-        if constexpr ((P4 & 1) == 0) softmax_phase(j);
-      }
-    }
-    if constexpr (P4 & 1) wait_vmem();
-    __syncthreads();
-  };
-  for (int p = 0; p < n_phases; p += 4) {
-    phase(p, std::integral_constant<int, 0>{});
-    phase(p + 1, std::integral_constant<int, 1>{});
-    if (p + 2 < n_phases) {
-      phase(p + 2, std::integral_constant<int, 2>{});
-      phase(p + 3, std::integral_constant<int, 3>{});
-    }
-  }
-
-  // ---- epilogue: O = O~ / l, L = m + ln l ------------------------------------
-  const float lt = half_swap_add(lsum);
-  const float inv = 1.0f / lt;
-  if (qrow < a.Nq) {
-    const size_t orow = (qhead + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d0 = db * 32 + 8 * a4 + 4 * g;
-        f32x4 ov = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
-                    oacc[db][4 * a4 + 3] * inv};
-        if constexpr (OUTF32) {
-          *(f32x4*)((float*)a.o + orow + d0) = ov;
-        } else {
-          *(bf16x4*)((__bf16*)a.o + orow + d0) = __builtin_convertvector(ov, bf16x4);
-        }
-      }
-    if (g == 0) a.lse[qhead + qrow] = (m + fast_log2(lt)) * kLn2;
-  }
-}
-
-template <int D, bool CAUSAL, bool OUTF32>
-static hipError_t launch_fwd_pp(FwdArgs a, hipStream_t stream) {
-  a.n_q_tiles = ceil_div(a.Nq, 256);
-  const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, OUTF32>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
-  return hipGetLastError();
-}
-
-// The two-group (ping-pong) bf16 kernel is used for d = 128 without the
-// causal mask from this many keys on. Its 256-row Q tiles and two-phase
-// pipeline pay a fill/drain cost per Q tile; measured on MI355X against the
-// 4-wave kernel (one box, N = 4K..32K, MHA and GQA): d = 128 non-causal
-// 2-3 % faster; d = 128 causal 4 % slower at 4K and within +-1.6 % from 8K;
-// d = 64 4-16 % slower at every length, so the other cases keep the 4-wave
-// kernel.
-constexpr int kPingPongMinKeys = 4096;
-
 // Causal d = 128 from this many keys on runs fwd_kernel with 8 wavefronts
-// (256-row Q tiles, one workgroup per CU): measured 1.3-3 % faster than 4
-// wavefronts from 8K keys and 2-14 % slower below (fewer, longer workgroups
-// balance worse on short causal rows).
-constexpr int kWide8MinKeys = 8192;
+// (256-row Q tiles, one workgroup per CU). Measured on MI355X against the
+// 4-wavefront kernel, both with three K buffers: 2 % faster at 16K keys,
+// 1.6 % slower at 8K (and 2-14 % slower below 8K with two buffers: fewer,
+// longer workgroups balance worse on short causal rows).
+constexpr int kWide8MinKeys = 16384;
 
 template <bool F32IN, int D, bool CAUSAL, bool OUTF32>
 static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
-  if constexpr (!F32IN && D == 128 && !CAUSAL) {
-    if (a.Nk >= kPingPongMinKeys) return launch_fwd_pp<D, CAUSAL, OUTF32>(a, stream);
-  }
   if constexpr (!F32IN && D == 128 && CAUSAL) {
     if (a.Nk >= kWide8MinKeys) {
       using T8 = FwdTile<false, D, 8>;

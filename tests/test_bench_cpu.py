@@ -30,7 +30,6 @@ def _write_counters(path, counter, per_kernel):
 
 def test_kernel_to_entry_point():
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4>(fa::FwdArgs)") == "fa_fwd"
-    assert bench._call_of("void fa::fwd_pp_kernel<128, true, false>(fa::FwdArgs)") == "fa_fwd"
     assert bench._call_of("void fa::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs)") == "fa_bwd"
     assert bench._call_of("void fa::bwd_dq_kernel<64, false>(fa::BwdArgs)") == "fa_bwd"
     assert bench._call_of("void fa::bwd_kernel<128, true, false, true>(fa::BwdArgs)") == "fa_bwd_atomic"

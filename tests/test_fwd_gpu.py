@@ -103,12 +103,13 @@ def test_fwd_scale_edge_cases(scale):
         assert np.max(np.abs(L - Lr)) <= L_TOL_BF16
 
 
-# Shapes with >= 4096 keys take the two-group (ping-pong) bf16 kernel; ragged
-# lengths, both head dims, GQA and Nq != Nk exercise its tiling and masks.
+# Longer key sequences: the three-K-buffer main loop over many phases, ragged
+# last tiles in both head dims, GQA and Nq != Nk (the 8-wavefront causal
+# kernel, from 16K keys, is covered by the long-sequence and workload tests).
 LONG_CASES = [
     (1, 2, 1, 4097, 4097, 128, True),
-    (1, 1, 1, 8300, 8300, 128, True),   # 8-wavefront causal kernel, ragged last Q tile
-    (1, 2, 2, 4500, 4500, 128, False),  # two-group kernel, ragged
+    (1, 1, 1, 8300, 8300, 128, True),   # ragged last Q tile
+    (1, 2, 2, 4500, 4500, 128, False),  # ragged
     (1, 2, 2, 4100, 4100, 64, True),
     (1, 2, 1, 333, 4200, 128, False),
     (1, 1, 1, 4096, 4096, 64, False),
