@@ -274,12 +274,38 @@ fwd_kernel(FwdArgs a) {
             const float ka = *(const float*)(Kt + tile_off<RC>(krow, (2 * kk + g) * 4));
             sacc[kb] = mfma_f32(ka, qf[kk], sacc[kb]);
           }
-        } else {
+        } else if constexpr (!DEEP) {
   #pragma unroll
           for (int kk = 0; kk < NQF; ++kk) {
             const bf16x8 ka = *(const bf16x8*)(Kt + koff[kk] + kb * 32 * ROWB);
             sacc[kb] = mfma_bf16(ka, qf[kk], sacc[kb]);
           }
+        }
+      }
+      if constexpr (DEEP) {
+        // The K operands of step kk + 1 are read before the products of step
+        // kk, and the schedule is pinned to that order: left to itself the
+        // compiler reads each operand just before its product and waits for
+        // it (measured 0.5-3 % slower on d = 128 shapes).
+        bf16x8 ka[2][NKB];
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) ka[0][kb] = *(const bf16x8*)(Kt + koff[0] + kb * 32 * ROWB);
+  #pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) {
+          if (kk + 1 < NQF) {
+  #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              ka[(kk + 1) & 1][kb] = *(const bf16x8*)(Kt + koff[kk + 1] + kb * 32 * ROWB);
+          }
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma_bf16(ka[kk & 1][kb], qf[kk], sacc[kb]);
+        }
+        // schedule: the first reads, then (next reads, this step's products)
+        __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+  #pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) {
+          if (kk + 1 < NQF) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
         }
       }
 
