@@ -193,10 +193,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int VROWB = D * 2, VRC = VROWB / 16, VTILEB = BC * VROWB, VCPW = VTILEB / (1024 * NW);  // bf16 V
   static_assert(KTILEB % (1024 * NW) == 0 && VTILEB % (1024 * NW) == 0, "tiles must split into whole wave loads");
 
+  // Three K buffers and two V buffers (56 KiB): K_j is fetched two steps
+  // before its scores, V_j one step before its product. Separate objects, so
+  // that the compiler can tell the prefetch into one from reads of another.
   __shared__ __attribute__((aligned(16))) char sK0[KTILEB];
   __shared__ __attribute__((aligned(16))) char sV0[VTILEB];
   __shared__ __attribute__((aligned(16))) char sK1[KTILEB];
   __shared__ __attribute__((aligned(16))) char sV1[VTILEB];
+  __shared__ __attribute__((aligned(16))) char sK2[KTILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,8 +222,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const size_t qhead = (size_t)(b * a.Hq + hq) * Nq;
   const size_t kvhead = (size_t)(b * a.Hkv + hkv) * Nk;
-  const char* __restrict__ Kh = (const char*)a.k + kvhead * KROWB;
-  const char* __restrict__ Vh = (const char*)a.v + kvhead * VROWB;
+  const char* __restrict__ Kh = uniform_ptr((const char*)a.k + kvhead * KROWB);
+  const char* __restrict__ Vh = uniform_ptr((const char*)a.v + kvhead * VROWB);
   const int nqb = ceil_div(Nq, 64), nkb = ceil_div(Nk, 64);
   // A wavefront whose rows all lie past the end (last query tile) stores
   // nothing; its block index is clamped to stay inside the scale array.
@@ -248,28 +252,44 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kv_end = kv_end_for(q0, BR, Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
 
-  // HBM -> LDS staging of one K tile (codes) and one V tile (bf16); rows
-  // past the end repeat the last row (their scores are masked).
-  auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
+  // HBM -> LDS staging of one K tile (codes) or one V tile (bf16): the
+  // tile's scalar base plus this lane's 32-bit offset, computed once (kept
+  // opaque so that the loads stay in the scalar-address form). In a tile that
+  // runs past the end of K/V (FULL false), rows past the end read the last
+  // row instead (their scores are masked).
+  int kld[KCPW], vld[VCPW];
+#pragma unroll
+  for (int u = 0; u < KCPW; ++u) {
+    const int idx = (wu * KCPW + u) * 64 + lane;
+    const int row = idx / KRC;
+    kld[u] = row * KROWB + (((idx % KRC) ^ swz<KRC>(row)) << 4);
+  }
+#pragma unroll
+  for (int u = 0; u < VCPW; ++u) {
+    const int idx = (wu * VCPW + u) * 64 + lane;
+    const int row = idx / VRC;
+    vld[u] = row * VROWB + (((idx % VRC) ^ swz<VRC>(row)) << 4);
+  }
+  auto issue = [&](auto full_tag, int jt, const char* __restrict__ Xh, const int* ld, auto ncpw, int rowb,
+                   char* Xt) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int CPWX = decltype(ncpw)::value;
     const int kv0 = jt * BC;
+    const char* Xb = uniform_ptr(Xh + (size_t)kv0 * rowb);
+    const unsigned last = (unsigned)(Nk - 1 - kv0);  // last row of K/V in this tile
 #pragma unroll
-    for (int u = 0; u < KCPW; ++u) {
-      const int cb = (wu * KCPW + u) * 64;
-      const int idx = cb + lane;
-      const int row = idx / KRC, pc = idx % KRC;
-      const int lc = pc ^ swz<KRC>(row);
-      const int grow = min(kv0 + row, Nk - 1);
-      load_lds_16(Kh + (size_t)grow * KROWB + lc * 16, Kt + cb * 16);
+    for (int u = 0; u < CPWX; ++u) {
+      unsigned ou = (unsigned)ld[u];
+      if (!FULL && kv0 + BC > Nk && ou / rowb > last) ou = last * rowb + ou % rowb;
+      asm volatile("" : "+v"(ou));
+      load_lds_16(Xb + ou, Xt + (wu * CPWX + u) * 64 * 16);
     }
-#pragma unroll
-    for (int u = 0; u < VCPW; ++u) {
-      const int cb = (wu * VCPW + u) * 64;
-      const int idx = cb + lane;
-      const int row = idx / VRC, pc = idx % VRC;
-      const int lc = pc ^ swz<VRC>(row);
-      const int grow = min(kv0 + row, Nk - 1);
-      load_lds_16(Vh + (size_t)grow * VROWB + lc * 16, Vt + cb * 16);
-    }
+  };
+  auto issue_k = [&](auto full_tag, int jt, char* Kt) __attribute__((always_inline)) {
+    issue(full_tag, jt, Kh, kld, std::integral_constant<int, KCPW>{}, KROWB, Kt);
+  };
+  auto issue_v = [&](auto full_tag, int jt, char* Vt) __attribute__((always_inline)) {
+    issue(full_tag, jt, Vh, vld, std::integral_constant<int, VCPW>{}, VROWB, Vt);
   };
 
   int koff[NKS][2];
@@ -293,10 +313,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   float m = -INFINITY;
   float lsum = 0.0f;
 
-  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt) __attribute__((always_inline)) {
+  // c: |scale| log2(e) times the Q block scale and this tile's K block scale
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt, float c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
-    const float c = a.c * sq * sk[jt];  // |scale| log2(e) times the two block scales
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -360,30 +380,84 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  auto step = [&](int jt, const char* Kt, const char* Vt, char* Kn, char* Vn) __attribute__((always_inline)) {
-    const int kv0 = jt * BC;
-    if (jt + 1 < n_kv) issue_tile(jt + 1, Kn, Vn);
-    const bool active = !CAUSAL || kv0 <= q0w + 31;
-    const bool need_mask = (CAUSAL && kv0 + BC - 1 > q0w) || (kv0 + BC > Nk);
-    if (active) {
-      if (need_mask)
-        body(std::true_type{}, jt, Kt, Vt);
+  // Loads are issued in the order K_0, V_0, K_1 (here), then V_{j+1},
+  // K_{j+2} at the top of step j, into K buffer j % 3 and V buffer j % 2.
+  // Step j ends by waiting for K_{j+1} and V_{j+1} (loads retire in issue
+  // order, so that is "at most the loads of K_{j+2} in flight"), then one
+  // barrier, after all of the wavefront's LDS reads have completed, so the
+  // loads of step j+1 may overwrite V_j and K_j. Steps before n_fast are
+  // unmasked for every wavefront (Q tiles start at multiples of BR), and
+  // both of their loads are whole tiles inside K/V; the others check
+  // everything and take the masked body.
+  constexpr int NTAIL = BR / BC;
+  const int n_fast = max(0, min(min(n_kv - NTAIL, n_kv - 2), Nk / BC - 2));
+  float c_next = 0.0f, c_cur = 0.0f;  // K block scale of the next tile; this tile's score factor
+  auto step = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Vn, char* Kn2)
+                  __attribute__((always_inline)) {
+    constexpr bool GENERIC = decltype(generic_tag)::value;
+    const bool has1 = !GENERIC || jt + 1 < n_kv;
+    const bool has2 = !GENERIC || jt + 2 < n_kv;
+    // The next tile's K block scale is loaded before this step's tile loads,
+    // so the end-of-step wait covers it and nothing waits on it earlier.
+    const float c = c_cur;
+    if (has1) c_next = sk[jt + 1];
+    if (has1) issue_v(std::bool_constant<!GENERIC>{}, jt + 1, Vn);
+    if (has2) issue_k(std::bool_constant<!GENERIC>{}, jt + 2, Kn2);
+    if constexpr (GENERIC) {
+      if (!CAUSAL || jt * BC <= q0w + 31) body(std::true_type{}, jt, Kt, Vt, c);
+      if (has2)
+        wait_vmem_n<KCPW>();
       else
-        body(std::false_type{}, jt, Kt, Vt);
+        wait_vmem_n<0>();
+    } else {
+      body(std::false_type{}, jt, Kt, Vt, c);
+      wait_vmem_n<KCPW>();
     }
-    wait_vmem();
-    __syncthreads();
+    c_cur = a.c * sq * c_next;
+    wait_lds();
+    lds_barrier();
   };
 
-  issue_tile(0, sK0, sV0);
-  wait_vmem();
-  __syncthreads();
-  int jt = 0;
-  for (; jt + 1 < n_kv; jt += 2) {
-    step(jt, sK0, sV0, sK1, sV1);
-    step(jt + 1, sK1, sV1, sK0, sV0);
+  c_next = sk[0];
+  issue_k(std::false_type{}, 0, sK0);
+  issue_v(std::false_type{}, 0, sV0);
+  if (n_kv > 1) {
+    issue_k(std::false_type{}, 1, sK1);
+    wait_vmem_n<KCPW>();
+  } else {
+    wait_vmem_n<0>();
   }
-  if (jt < n_kv) step(jt, sK0, sV0, sK1, sV1);
+  __syncthreads();
+  c_cur = a.c * sq * c_next;
+  // Main loop unrolled over the six (K buffer, V buffer) phases, so that every
+  // buffer is a compile-time choice; it can leave after any phase.
+  int jt = 0;
+  if (n_fast > 0) {
+    while (true) {
+      step(std::false_type{}, jt, sK0, sV0, sV1, sK2);
+      if (++jt >= n_fast) break;
+      step(std::false_type{}, jt, sK1, sV1, sV0, sK0);
+      if (++jt >= n_fast) break;
+      step(std::false_type{}, jt, sK2, sV0, sV1, sK1);
+      if (++jt >= n_fast) break;
+      step(std::false_type{}, jt, sK0, sV1, sV0, sK2);
+      if (++jt >= n_fast) break;
+      step(std::false_type{}, jt, sK1, sV0, sV1, sK0);
+      if (++jt >= n_fast) break;
+      step(std::false_type{}, jt, sK2, sV1, sV0, sK1);
+      if (++jt >= n_fast) break;
+    }
+  }
+  for (; jt < n_kv; ++jt) {
+    switch (jt % 6) {
+      case 0: step(std::true_type{}, jt, sK0, sV0, sV1, sK2); break;
+      case 1: step(std::true_type{}, jt, sK1, sV1, sV0, sK0); break;
+      case 2: step(std::true_type{}, jt, sK2, sV0, sV1, sK1); break;
+      case 3: step(std::true_type{}, jt, sK0, sV1, sV0, sK2); break;
+      case 4: step(std::true_type{}, jt, sK1, sV0, sV1, sK0); break;
+      default: step(std::true_type{}, jt, sK2, sV1, sV0, sK1); break;
+    }
+  }
 
   const float lt = half_swap_add(lsum);
   const float inv = 1.0f / lt;
