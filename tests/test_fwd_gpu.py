@@ -45,6 +45,10 @@ CASES = [
     (1, 2, 2, 333, 65, 64, False),
     (2, 8, 2, 512, 512, 128, True),
     (1, 1, 1, 1000, 1000, 128, True),
+    # non-causal d=128 with 1 and 5 unmasked steps: the three-buffer main
+    # loop leaves after phases 1 and 5 of its six
+    (1, 2, 2, 64, 192, 128, False),
+    (1, 2, 1, 200, 448, 128, False),
 ]
 
 
