@@ -611,7 +611,7 @@ def main():
     avg_fwd = float(np.mean(per_call[:, 0]))
     avg_bwd = float(np.mean(per_call[:, 1]))
     if avg_bwd >= avg_fwd:
-        dom = {"kernel": "fa_bwd (bwd_preprocess_kernel + bwd_dkdv_kernel + bwd_dq_kernel, one call)", "flops": bf,
+        dom = {"kernel": "fa_bwd (bwd_dq_kernel with D + bwd_dkdv_kernel, one call)", "flops": bf,
                "ms": avg_bwd, "traffic": measured_traffic("fa_bwd")}
     else:
         dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd, "traffic": measured_traffic("fa_fwd")}

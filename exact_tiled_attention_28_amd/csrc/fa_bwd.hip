@@ -1,7 +1,11 @@
 // fa_bwd.hip — exact attention backward for gfx950, FlashAttention-2 order.
 //
 // Method (page "6.2 FlashAttention V2 chi tiết", section 7; CSDN
-// FlashAttention-2 article, "3.1.2 反向传播公式解析", "并行性 / 反向传播"):
+// FlashAttention-2 article, "3.1.2 反向传播公式解析", "并行性 / 反向传播").
+// fa_bwd (two passes, no atomics): bwd_dq_kernel (Q-outer) forms
+// D = rowsum(dO o O) once per row (section 7.3), stores it, and sums dQ in
+// registers; then bwd_dkdv_kernel (K/V-outer) forms dK and dV, reading D.
+// fa_bwd_atomic (single pass, the scheme the pages describe first):
 //   1. a separate preprocess kernel computes D = rowsum(dO o O) once and
 //      zeroes the fp32 dQ accumulator (page 6.2, section 7.3);
 //   2. the main kernel gives each workgroup one K/V column block j; it walks
@@ -834,7 +838,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   // Rows past the end get L = +inf, so their P (and dS) is 0.
   const float l2 = qrow < Nq ? a.lse[qhead + qrow] * kLog2e : INFINITY;
-  const float dq_d = qrow < Nq ? a.dvec[qhead + qrow] : 0.0f;
+  // D = rowsum(dO o O) of this lane's row (page 6.2, section 7.3), formed
+  // here from the dO fragments already in registers and the same head-dim
+  // ranges of O (half a row per lane, the other half in lane l ^ 32), and
+  // stored for the dK/dV pass, which runs after this one. Rows past the end
+  // get D = 0 and store nothing.
+  float dq_d = 0.0f;
+  {
+    float acc = 0.0f;
+    if (qrow < Nq) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const f32x8 df = __builtin_convertvector(dof[kk], f32x8);
+        f32x8 of;
+        if (a.o_f32) {
+          const float* Orow = (const float*)a.o + (qhead + qrow) * D + kk * 16 + 8 * g;
+          const f32x4 lo = *(const f32x4*)Orow;
+          const f32x4 hi = *(const f32x4*)(Orow + 4);
+          of = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          const u32x4 ov = *(const u32x4*)((const __bf16*)a.o + (qhead + qrow) * D + kk * 16 + 8 * g);
+          of = __builtin_convertvector(__builtin_bit_cast(bf16x8, ov), f32x8);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(df[e], of[e], acc);
+      }
+    }
+    dq_d = half_swap_add(acc);
+    if (qrow < Nq && g == 0) a.dvec[qhead + qrow] = dq_d;
+  }
 
   const int kv_end = kv_end_for(q0, BR, Nk, CAUSAL);
   const int n_kv = ceil_div(kv_end, BC);
@@ -1036,60 +1068,52 @@ static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Two-pass backward (fa_bwd): the dQ pass first, which also forms D and
+// stores it, then the dK/dV pass, which reads D. The single-pass atomic
+// backward (fa_bwd_atomic) keeps the separate preprocess kernel, which also
+// zeroes its dQ accumulator.
 template <int D, bool CAUSAL, bool GF32>
-static hipError_t launch_bwd_all(const BwdArgs& a, bool o_f32, bool atomic_dq, hipStream_t s) {
-  const long long rows = (long long)a.B * a.Hq * a.Nq;
-  const long long threads = rows * (D / 8);
-  const unsigned pblocks = (unsigned)((threads + 255) / 256);
-  const __bf16* dout = (const __bf16*)a.dout;
-  if (o_f32) {
-    if (atomic_dq)
+static hipError_t launch_bwd_all(const BwdArgs& a0, bool o_f32, bool atomic_dq, hipStream_t s) {
+  BwdArgs a = a0;
+  a.o_f32 = o_f32 ? 1 : 0;
+  if (atomic_dq) {
+    const long long rows = (long long)a.B * a.Hq * a.Nq;
+    const long long threads = rows * (D / 8);
+    const unsigned pblocks = (unsigned)((threads + 255) / 256);
+    const __bf16* dout = (const __bf16*)a.dout;
+    if (o_f32)
       hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, true>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
     else
-      hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
-  } else {
-    if (atomic_dq)
       hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, true>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
-    else
-      hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (atomic_dq) return launch_bwd_main<D, CAUSAL, GF32, true>(a, s);
-  e = launch_bwd_dkdv<D, CAUSAL, GF32>(a, s);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq<D, CAUSAL>(a, s);
-}
-
-// Packed variable-length batch: the D preprocess runs over the Hq x total_q
-// rows as one flat array; the dK/dV and dQ grids cover the longest sequence
-// and workgroups past their sequence's end exit at once.
-template <int D, bool CAUSAL, bool GF32>
-static hipError_t launch_bwd_varlen_t(const BwdArgs& a, bool o_f32, hipStream_t s) {
-  const long long rows = (long long)a.Hq * a.total_q;
-  const long long threads = rows * (D / 8);
-  const unsigned pblocks = (unsigned)((threads + 255) / 256);
-  const __bf16* dout = (const __bf16*)a.dout;
-  if (pblocks > 0) {
-    if (o_f32)
-      hipLaunchKernelGGL((bwd_preprocess_kernel<D, true, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
-    else
-      hipLaunchKernelGGL((bwd_preprocess_kernel<D, false, false>), dim3(pblocks), dim3(256), 0, s, dout, a.o, a.dvec, a.dq, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_bwd_main<D, CAUSAL, GF32, true>(a, s);
   }
+  hipError_t e = launch_bwd_dq<D, CAUSAL>(a, s);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dkdv<D, CAUSAL, GF32>(a, s);
+}
+
+// Packed variable-length batch: the dQ pass (which forms and stores D) and
+// then the dK/dV pass; both grids cover the longest sequence and workgroups
+// past their sequence's end exit at once. Rows of D that belong to no
+// sequence are never read.
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_varlen_t(const BwdArgs& a0, bool o_f32, hipStream_t s) {
+  BwdArgs a = a0;
+  a.o_f32 = o_f32 ? 1 : 0;
   {
-    using T = DkdvTile<D>;
-    auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true>;
-    const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
+    const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
     if (blocks > 0) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
-  if (blocks > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  using T = DkdvTile<D>;
+  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true>;
+  const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
+  if (blocks > 0) hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, s, a);
   return hipGetLastError();
 }
 

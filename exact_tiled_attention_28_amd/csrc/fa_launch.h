@@ -42,6 +42,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;  // D = rowsum(dO o O), fp32 [B][Hq][Nq]
+  int o_f32;    // O is fp32 (else bf16)
   int B, Hq, Hkv, G, Nq, Nk;
   float scale;
   float c;  // scale * log2(e)

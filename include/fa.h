@@ -95,11 +95,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   dQ = scale * dS K; dK = scale * dS^T Q;
  * with dK, dV summed over the query heads of each K/V head group.
  *
- * Scheme: D is computed once by a preprocess kernel (section 7.3); dK and dV
- * by workgroups that each own one K/V column block (section 7.2); dQ by a
- * second pass over Q tiles (the "two-pass" alternative to atomics that
- * section 7.2 names), so no atomics are used and every output is
- * deterministic. fa_bwd_atomic below is the single-pass variant.
+ * Scheme: a pass over Q tiles forms D once per row (section 7.3) and dQ
+ * (the "two-pass" alternative to atomics that section 7.2 names); then dK
+ * and dV by workgroups that each own one K/V column block (section 7.2),
+ * reading D. No atomics are used and every output is deterministic.
+ * fa_bwd_atomic below is the single-pass variant.
  *
  *   q, dout  [B][Hq][Nq][d] in_dtype (must be FA_DTYPE_BF16), read only
  *   k, v     [B][Hkv][Nk][d] in_dtype, read only
