@@ -138,3 +138,48 @@ def test_bwd_two_pass_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+BF16_O_CASES = [
+    (1, 4, 2, 300, 300, 128, True),
+    (1, 2, 2, 129, 200, 64, False),
+    (2, 2, 1, 257, 257, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_O_CASES,
+                         ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}"
+                              for c in BF16_O_CASES])
+def test_bwd_with_bf16_o(case):
+    """fa_bwd given the bf16 O of the forward (the timed configuration): D must
+    be rowsum(dO o O) of that O, and the gradients must match the oracle up to
+    the rounding bound plus the exact effect of D's change: with
+    dD_i = rowsum(dO_i o (O16_i - O_i)), dS_ij moves by -P_ij dD_i, so dQ_i
+    moves by -s dD_i (P K)_i and dK_j by -s sum_i P_ij dD_i Q_i; dV does not
+    move."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    announce(f"bwd with bf16 O {case}")
+    inp = gen(500 + Nq + d, B, Hq, Hkv, Nq, Nk, d, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    q, k, v, do = upload(inp)
+    o16, lse = binding.forward(q, k, v, scale, causal, out_dtype=torch.bfloat16)
+    dq, dk, dv, dvec = binding.backward(q, k, v, o16, lse, do, scale, causal, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O16 = host(o16).astype(np.float64)
+    dQ, dK, dV, Dv = host(dq), host(dk), host(dv), host(dvec)
+    assert np.max(np.abs(Dv - oracle.row_dot(inp.do, O16))) <= 1e-4
+    dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    bq, bk, bv = rounding_bounds(inp, scale, causal)
+    qq, kk, vv, dd = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            P = oracle.probabilities_head(qq[b, h], kk[b, g], scale, causal)
+            dD = oracle.row_dot(dd[b, h], O16[b, h] - P @ vv[b, g])
+            bq[b, h] += abs(scale) * np.abs(dD)[:, None] * np.abs(P @ kk[b, g])
+            bk[b, g] += abs(scale) * P.T @ (np.abs(dD)[:, None] * np.abs(qq[b, h]))
+    assert np.all(np.abs(dQ - dQr) <= TOL + bq), "dQ"
+    assert np.all(np.abs(dK - dKr) <= TOL + bk), "dK"
+    assert np.all(np.abs(dV - dVr) <= TOL + bv), "dV"
