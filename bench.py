@@ -651,6 +651,11 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "avg_launch_ms": round(dom["ms"], 4)},
     }
+    # The other named workloads, each pass timed on its own after the step
+    # (context for the same run; not part of value).
+    out["other_workloads"] = {name: {k2: v2 for k2, v2 in time_workload(WORKLOADS[name], 10, 3).items()
+                                     if k2 != "workload"}
+                              for name in WORKLOADS if name != STEP_WORKLOAD}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(out), flush=True)
@@ -672,7 +677,11 @@ def copy_calibration(mib):
 
 def bench_one(args):
     """Time one named workload's pass (fwd or bwd); prints one JSON line."""
-    w = WORKLOADS[args.workload]
+    print(json.dumps(time_workload(WORKLOADS[args.workload], args.steps, args.warmup)), flush=True)
+
+
+def time_workload(w, steps, warmup):
+    """Median time of one named workload's pass (fwd or bwd), as a dict."""
     inp, q, k, v, do = device_inputs(w, with_do=w.passes == "bwd")
     step = Step(w, q, k, v, do if do is not None else q)
     if w.passes == "bwd":
@@ -683,13 +692,13 @@ def bench_one(args):
         calls, fl = [step.fwd], fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
         eb = 4 if w.dtype == "f32" else 2
         by = fwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim, eb, eb)
-    per_step, _, _ = time_calls(step, calls, args.steps, args.warmup)
+    per_step, _, _ = time_calls(step, calls, steps, warmup)
     ms = float(np.median(per_step))
     tf = fl / (ms * 1e-3) / 1e12
-    print(json.dumps({"workload": w.name, "ms": round(ms, 4), "ms_min": round(float(per_step.min()), 4),
-                      "tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / MI355X_BF16_PEAK_TFLOPS, 2),
-                      "gbps_algorithmic": round(by / (ms * 1e-3) / 1e9, 1),
-                      "pct_of_hbm": round(100 * by / (ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 2)}), flush=True)
+    return {"workload": w.name, "ms": round(ms, 4), "ms_min": round(float(per_step.min()), 4),
+            "tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / MI355X_BF16_PEAK_TFLOPS, 2),
+            "gbps_algorithmic": round(by / (ms * 1e-3) / 1e9, 1),
+            "pct_of_hbm": round(100 * by / (ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 2)}
 
 
 if __name__ == "__main__":
