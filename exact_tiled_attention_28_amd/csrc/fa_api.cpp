@@ -1,5 +1,6 @@
 // fa_api.cpp — the C ABI declared in include/fa.h: validate on the host,
 // pick the kernel instantiation, launch on the caller's stream, return.
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -21,6 +22,16 @@ int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return FA_OK;
   return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
+
+// Multiplier of the raw scores in the bf16/fp32 forward kernels' exp2
+// arguments, |scale| log2(e) (a negative scale negates Q instead). A zero
+// scale is raised to the smallest normal float: the kernels set masked
+// scores to -inf and rely on -inf * c staying -inf (0 * -inf would be NaN),
+// so that exp2 yields 0 with no per-element test. Scaled scores of any
+// realistic size are then far below fp32 resolution next to 0 and 1, so
+// every visible key gets probability exactly 1 before normalisation, as
+// with a zero scale.
+float fwd_exp2_mult(float scale) { return std::fmax(std::fabs(scale) * 1.4426950408889634f, FLT_MIN); }
 
 }  // namespace
 
@@ -44,7 +55,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.G = n_q_heads / n_kv_heads;
   a.Nq = seqlen_q;
   a.Nk = seqlen_k;
-  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.c = fwd_exp2_mult(scale);
   a.neg = scale < 0.0f;
   hipError_t e = fa::launch_fwd(a, head_dim, in_dtype == FA_DTYPE_F32, causal != 0, out_dtype == FA_DTYPE_F32,
                                 (hipStream_t)stream);
@@ -72,7 +83,7 @@ int fa_fwd_persistent(const void* q, const void* k, const void* v, void* o, floa
   a.G = n_q_heads / n_kv_heads;
   a.Nq = seqlen_q;
   a.Nk = seqlen_k;
-  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.c = fwd_exp2_mult(scale);
   a.neg = scale < 0.0f;
   a.sched = sched;
   hipError_t e = fa::launch_fwd_persistent(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
@@ -161,7 +172,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   a.G = n_q_heads / n_kv_heads;
   a.Nq = max_seqlen_q;
   a.Nk = max_seqlen_k;
-  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.c = fwd_exp2_mult(scale);
   a.neg = scale < 0.0f;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;

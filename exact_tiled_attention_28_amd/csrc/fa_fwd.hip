@@ -239,7 +239,10 @@ fwd_kernel(FwdArgs a) {
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     float m = -INFINITY;  // reference max, log2 units (scaled scores)
     float lsum = 0.0f;    // running sum over this half-wave's keys
-    const float c = a.c;
+    const float c = a.c;  // > 0: a zero scale arrives as the smallest normal float
+    // Last key this lane's query row may see (rows past the end of Q are
+    // computed like the last row and not stored).
+    const int last_key = CAUSAL ? min(qrow, Nk - 1) : Nk - 1;
 
     // Per-lane LDS byte offsets of the MFMA operand fetches, computed once.
     // The swizzle of a row depends only on the row modulo 8, so moving by
@@ -310,15 +313,17 @@ fwd_kernel(FwdArgs a) {
       }
 
       // ---- mask (diagonal-crossing or ragged tiles only) ------------------------
+      // Key kv0 + kb*32 + 8*(r/4) + 4g + r%4 is visible iff it is at most
+      // last_key; with the lane's part folded into t, each test compares a
+      // constant with t. Masked scores become -inf, which the exp2 below
+      // (multiplier c > 0) turns into probability 0.
       if constexpr (MASK) {
+        const int t = last_key - kv0 - 4 * g;
   #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = key < Nk && (!CAUSAL || key <= qrow);
-            sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= t) ? sacc[kb][r] : -INFINITY;
       }
 
       // ---- online softmax ---------------------------------------------------------
@@ -341,8 +346,7 @@ fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
-          if constexpr (MASK) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
+          const float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
           sacc[kb][r] = p;
           rs += p;
         }
