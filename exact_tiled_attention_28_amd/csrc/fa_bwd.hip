@@ -29,6 +29,7 @@
 // read by transpose reads, then added to HBM with fp32 atomics (lanes cover
 // contiguous head-dim columns, so each atomic instruction touches whole
 // cache lines).
+#include <climits>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -627,7 +628,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16(*(const bf16x8*)(qRows + roff[kk]), kf[kk], s);
     }
-    // P = exp2(S c - L log2 e)
+    // P = exp2(S c - L log2 e). Masked: query q0 + 32h + 8*a4 + 4g + e sees
+    // this lane's key iff 8*a4 + e >= tq (no query if the key is past the end
+    // of K, every query without the causal mask).
+    const int tq = key >= Nk ? INT_MAX : (CAUSAL ? key - q0 - 32 * h - 4 * g : INT_MIN);
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int r0 = h * 32 + 8 * a4 + 4 * g;
@@ -635,10 +639,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float p = fast_exp2(fmaf(s[4 * a4 + e], c, -lv[e]));
-        if constexpr (MASK) {
-          const bool vis = key < Nk && (!CAUSAL || key <= q0 + r0 + e);
-          p = vis ? p : 0.0f;
-        }
+        if constexpr (MASK) p = (8 * a4 + e >= tq) ? p : 0.0f;
         s[4 * a4 + e] = p;
       }
     }
@@ -926,6 +927,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
   const float c = a.c;
+  // Last key this lane's query row may see (rows past the end of Q are
+  // computed like the last row and not stored).
+  const int last_key = CAUSAL ? min(qrow, Nk - 1) : Nk - 1;
 
   // One K/V tile, 32 keys at a time (block kb): S^T and dP^T for the block,
   // then dS^T, then its share of dQ^T += K^T dS^T, so only one block's S^T,
@@ -942,15 +946,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         dpacc = mfma_bf16(*(const bf16x8*)(Vt + koff[kk] + kb * 32 * ROWB), dof[kk], dpacc);
       }
       // P^T = exp2(S^T c - L log2 e), dS^T = P^T o (dP^T - D)
+      // Masked: key kv0 + kb*32 + 8*(r/4) + 4g + r%4 is visible iff it is at
+      // most last_key, i.e. iff 8*(r/4) + r%4 <= tk.
+      const int tk = last_key - kv0 - kb * 32 - 4 * g;
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(sacc[r], c, -l2));
-        if constexpr (MASK) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < Nk && (!CAUSAL || key <= qrow);
-          p = vis ? p : 0.0f;
-        }
+        if constexpr (MASK) p = (8 * (r >> 2) + (r & 3) <= tk) ? p : 0.0f;
         dsv[r] = p * (dpacc[r] - dq_d);
       }
       // dQ^T += K^T dS^T: slot (g, v) of step t holds key 16t + 8*(v/4) + 4g + v%4

@@ -19,6 +19,7 @@
 //     codes by v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 accumulate) and
 //     scaled by the two block scales in fp32 before the softmax; P V stays in
 //     bf16 as in fa_fwd.
+#include <cfloat>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -312,8 +313,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY;
   float lsum = 0.0f;
+  // Last key this lane's query row may see (rows past the end of Q are
+  // computed like the last row and not stored).
+  const int last_key = CAUSAL ? min(qrow, Nk - 1) : Nk - 1;
 
-  // c: |scale| log2(e) times the Q block scale and this tile's K block scale
+  // c: |scale| log2(e) times the Q block scale and this tile's K block scale,
+  // raised to at least the smallest normal float (a zero scale then gives
+  // every visible key probability exactly 1 before normalisation)
   auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt, float c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
@@ -329,15 +335,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf[ks], sacc[kb], 0, 0, 0, 0, 0, 0);
       }
     }
+    // Key kv0 + kb*32 + 8*(r/4) + 4g + r%4 is visible iff it is at most
+    // last_key: one compare of a constant with t per score. Masked scores
+    // become -inf, which exp2 below turns into 0 (c is at least the smallest
+    // normal float, so -inf * c stays -inf).
     if constexpr (MASK) {
+      const int t = last_key - kv0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < Nk && (!CAUSAL || key <= qrow);
-          sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) <= t) ? sacc[kb][r] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -358,8 +365,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
-        if constexpr (MASK) p = (sacc[kb][r] == -INFINITY) ? 0.0f : p;
+        const float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
         sacc[kb][r] = p;
         rs += p;
       }
@@ -413,7 +419,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       body(std::false_type{}, jt, Kt, Vt, c);
       wait_vmem_n<KCPW>();
     }
-    c_cur = a.c * sq * c_next;
+    c_cur = fmaxf(a.c * sq * c_next, FLT_MIN);
     wait_lds();
     lds_barrier();
   };
@@ -428,7 +434,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     wait_vmem_n<0>();
   }
   __syncthreads();
-  c_cur = a.c * sq * c_next;
+  c_cur = fmaxf(a.c * sq * c_next, FLT_MIN);
   // Main loop unrolled over the six (K buffer, V buffer) phases, so that every
   // buffer is a compile-time choice; it can leave after any phase.
   int jt = 0;
