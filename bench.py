@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip timing the other named workloads after the step (profiled runs of the step use this)")
     p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
     p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
@@ -653,9 +655,10 @@ def main():
     }
     # The other named workloads, each pass timed on its own after the step
     # (context for the same run; not part of value).
-    out["other_workloads"] = {name: {k2: v2 for k2, v2 in time_workload(WORKLOADS[name], 10, 3).items()
-                                     if k2 != "workload"}
-                              for name in WORKLOADS if name != STEP_WORKLOAD}
+    if not args.no_others:
+        out["other_workloads"] = {name: {k2: v2 for k2, v2 in time_workload(WORKLOADS[name], 10, 3).items()
+                                         if k2 != "workload"}
+                                  for name in WORKLOADS if name != STEP_WORKLOAD}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(out), flush=True)
