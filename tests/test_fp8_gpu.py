@@ -138,6 +138,7 @@ FWD_CASES = [
     (1, 3, 1, 70, 600, False, True, 0, None),
     (1, 2, 2, 200, 200, True, True, 2, -0.1),
     (1, 2, 1, 64, 64, False, True, 0, 0.0),
+    (1, 2, 1, 200, 200, True, True, 0, 0.0),  # zero scale on masked diagonal tiles
     # longer rows: several passes of the six-phase main loop, leaving after
     # phases 1, 4 and 5
     (1, 2, 1, 200, 1000, False, True, 0, None),

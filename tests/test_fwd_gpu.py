@@ -96,13 +96,17 @@ def test_fwd_bf16_output_rounding():
     assert np.max(np.abs(L - Lr)) <= L_TOL_BF16
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
-def test_fwd_scale_edge_cases(scale):
-    announce(f"fwd scale {scale}")
-    inp = gen(8, 1, 2, 2, 200, 200, 64)
+def test_fwd_scale_edge_cases(scale, d):
+    # A zero scale also checks the masked tiles' -inf scores under the
+    # kernels' smallest-normal multiplier (probability 0, not NaN).
+    announce(f"fwd scale {scale} d {d}")
+    inp = gen(8, 1, 2, 2, 200, 200, d)
     for causal in (False, True):
         O, L = run_fwd(inp, scale, causal)
         Or, Lr = oracle.forward(inp.q, inp.k, inp.v, scale, causal)
+        assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
         assert np.max(np.abs(O - Or)) <= O_TOL_BF16
         assert np.max(np.abs(L - Lr)) <= L_TOL_BF16
 
