@@ -33,8 +33,6 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 // C += A * B, 32x32 output, K = 16, bf16 operands, fp32 accumulate.
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -98,22 +96,15 @@ __device__ __forceinline__ int tile_off(int row, int byte_in_row) {
   return row * (ROW_CHUNKS * 16) + (((c ^ swz<ROW_CHUNKS>(row)) << 4) | (byte_in_row & 15));
 }
 
-// Transpose read of 4 bf16 down a column of a swizzled bf16 LDS tile
-// (ds_read_b64_tr_b16). Each lane supplies the address of 4 consecutive
-// columns of one row; within each 16-lane block the hardware hands lane i
-// element i%4 of lane 4e + i/4 as its element e (checked on gfx950). With
-// lane j of block b pointing at row row_base + j/4, columns
-// col_base + 16*(b%2) + 4*(j%4), lane i of block b receives rows
-// row_base + e (e = 0..3) of column col_base + 16*(b%2) + i.
-template <int RC>
-__device__ __forceinline__ short4v tr_read(const char* tile, int row_base, int col_base_elems, int lane) {
-  const int j = lane & 15;
-  const int row = row_base + (j >> 2);
-  const int col = col_base_elems + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const char* p = tile + tile_off<RC>(row, col * 2);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(p));
-}
-
+// Transpose reads of 4 bf16 down a column of a swizzled bf16 LDS tile
+// (ds_read_b64_tr_b16, which the kernels issue with per-lane offsets
+// computed once): each lane supplies the address of 4 consecutive columns of
+// one row; within each 16-lane block the hardware hands lane i element i%4
+// of lane 4e + i/4 as its element e (checked on gfx950). With lane j of
+// block b pointing at row row_base + j/4, columns col_base + 16*(b%2) +
+// 4*(j%4), lane i of block b receives rows row_base + e (e = 0..3) of column
+// col_base + 16*(b%2) + i.
+//
 // Two transpose reads joined into one 8-element MFMA operand.
 __device__ __forceinline__ bf16x8 cat4(short4v a, short4v b) {
   typedef __attribute__((ext_vector_type(8))) short short8v;
@@ -138,18 +129,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
   return (const char*)(((uint64_t)hi << 32) | lo);
-}
-
-// Word 3 of a raw buffer resource for gfx9-family GPUs (gfx950 included):
-// 32-bit data format, no swizzle; with stride 0 the resource is a plain
-// byte-addressed range of num_records bytes.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-// HBM -> LDS through a buffer resource (buffer_load_dwordx4 ... lds): lane l
-// fetches the 16 bytes at byte voff of the resource into
-// lds_wave_base + 16*l. lds_wave_base must be uniform across the wavefront.
-__device__ __forceinline__ void load_lds_16_buf(__amdgpu_buffer_rsrc_t rs, int voff, void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_wave_base, 16, voff, 0, 0, 0);
 }
 
 // Wait until this wavefront's outstanding vector-memory loads (including the
