@@ -610,20 +610,21 @@ fwd_kernel(FwdArgs a) {
   }
 }
 
-// Causal d = 128 from this many keys on runs fwd_kernel with 8 wavefronts
-// (256-row Q tiles, one workgroup per CU). Measured on MI355X against the
-// 4-wavefront kernel, both with three K buffers: 2 % faster at 16K keys,
-// 1.6 % slower at 8K (and 2-14 % slower below 8K with two buffers: fewer,
-// longer workgroups balance worse on short causal rows).
+// Causal bf16 input from this many keys on runs fwd_kernel with 8
+// wavefronts (256-row Q tiles sharing each K/V tile). Measured on MI355X
+// against the 4-wavefront kernel: d = 128 (both with three K buffers) 2 %
+// faster at 16K keys, 1.6 % slower at 8K (and 2-14 % slower below 8K with
+// two buffers: fewer, longer workgroups balance worse on short causal rows);
+// d = 64 3.3-3.4 % faster at 16K, 2.4 % at 32K.
 constexpr int kWide8MinKeys = 16384;
-// d = 128 without the causal mask takes the 8-wavefront kernel from this
-// many keys on: measured 3.6 %
-// faster at 8K, 5 % at 16K, 2-5 % at 32K (MHA and GQA), level at 4K.
+// Without the causal mask the 8-wavefront kernel runs from this many keys
+// on: measured at d = 128 3.6 % faster at 8K, 5 % at 16K, 2-5 % at 32K (MHA
+// and GQA), level at 4K; at d = 64 5 % faster at 8K and 16K, 2.3 % at 32K.
 constexpr int kWide8MinKeysNonCausal = 8192;
 
 template <bool F32IN, int D, bool CAUSAL, bool OUTF32>
 static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {
-  if constexpr (!F32IN && D == 128) {
+  if constexpr (!F32IN) {
     if (a.Nk >= (CAUSAL ? kWide8MinKeys : kWide8MinKeysNonCausal)) {
       using T8 = FwdTile<false, D, 8>;
       a.n_q_tiles = ceil_div(a.Nq, T8::BR);

@@ -113,7 +113,8 @@ def test_fwd_scale_edge_cases(scale, d):
 
 # Longer key sequences: the three-K-buffer main loop over many phases, ragged
 # last tiles in both head dims, GQA and Nq != Nk (the 8-wavefront causal
-# kernel, from 16K keys, is covered by the long-sequence and workload tests).
+# kernel at d = 128, from 16K keys, is covered by the long-sequence and
+# workload tests).
 LONG_CASES = [
     (1, 2, 1, 4097, 4097, 128, True),
     (1, 1, 1, 8300, 8300, 128, True),   # ragged last Q tile
@@ -125,6 +126,10 @@ LONG_CASES = [
     # 256-row Q tiles and a ragged last K/V tile, MHA and GQA
     (1, 1, 1, 300, 8300, 128, False),
     (1, 4, 1, 520, 8200, 128, False),
+    # the same kernel at d = 64: ragged Q tiles without the mask, and a
+    # causal run from 16384 keys with a ragged last tile
+    (1, 2, 1, 300, 8300, 64, False),
+    (1, 1, 1, 16400, 16400, 64, True),
 ]
 
 
