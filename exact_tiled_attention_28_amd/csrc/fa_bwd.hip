@@ -773,9 +773,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 // S^T = K Q^T and dP^T = V dO^T take Q and dO as register B operands, L and D
 // are per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from the
 // accumulator registers and K^T by transpose reads of the K tile.
-template <int D, bool CAUSAL, bool VARLEN = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdArgs a) {
-  constexpr int NW = 4, BR = 32 * NW, BC = 64, NKB = BC / 32;
+template <int D, bool CAUSAL, bool VARLEN = false, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdArgs a) {
+  constexpr int BR = 32 * NW, BC = 64, NKB = BC / 32;
   constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB, CPW = TILEB / (1024 * NW);
   constexpr int NKK = D / 16, NDB = D / 32;
   static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole wave loads");
@@ -1064,8 +1064,22 @@ static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// At d = 128 the dQ pass runs with 8 wavefronts (256-row Q tiles sharing
+// each K/V tile, one workgroup per CU) from this many keys on. Measured on
+// MI355X against 4 wavefronts, whole backward: +1.0-1.8 % at 8K keys,
+// +1.7-4.1 % at 16K-32K (causal and not, MHA and GQA), -0.5 to +1.3 % at
+// 4K; at d = 64 within +-1 % at 16K, so d = 64 keeps 4 wavefronts.
+constexpr int kDq8MinKeys = 8192;
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (a.Nk >= kDq8MinKeys) {
+      const long long blocks8 = (long long)a.B * a.Hq * ceil_div(a.Nq, 256);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, 8>), dim3((unsigned)blocks8), dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();

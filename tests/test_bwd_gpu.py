@@ -101,6 +101,28 @@ def test_bwd_parity(case, atomic_dq):
     assert np.max(np.abs(dV.sum(axis=2) - ref)) <= 0.05 + 1e-3 * np.max(np.abs(ref))
 
 
+# From 8192 keys the d = 128 dQ pass runs with 8 wavefronts (256-row Q
+# tiles): a causal run with a ragged last Q tile, and ragged Q tiles without
+# the mask (Nq = 300).
+WIDE_DQ_CASES = [(1, 1, 1, 8300, 8300, 128, True), (1, 2, 1, 300, 8300, 128, False)]
+
+
+@pytest.mark.parametrize("case", WIDE_DQ_CASES,
+                         ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}" for c in WIDE_DQ_CASES])
+def test_bwd_wide_dq_parity(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    announce(f"bwd wide dQ {case}")
+    inp = gen(500 + Nq + d, B, Hq, Hkv, Nq, Nk, d, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L, dQ, dK, dV, Dv = run_fwd_bwd(inp, scale, causal)
+    dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    bq, bk, bv = rounding_bounds(inp, scale, causal)
+    assert np.all(np.abs(dQ - dQr) <= TOL + bq), "dQ"
+    assert np.all(np.abs(dK - dKr) <= TOL + bk), "dK"
+    assert np.all(np.abs(dV - dVr) <= TOL + bv), "dV"
+    assert np.max(np.abs(Dv - oracle.row_dot(inp.do, O))) <= 1e-4
+
+
 @pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic"])
 def test_bwd_bf16_grads(atomic_dq):
     announce(f"bwd bf16 grads atomic_dq={atomic_dq}")
