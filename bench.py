@@ -30,6 +30,9 @@ import time
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+# Copy-calibrated HBM bytes per launch of the step's calls, written by
+# --summarize-profiles from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "fa_step_b8_h16_n2048_d128_hbm_bytes.json")
 sys.path.insert(0, ROOT)
 
 from exact_tiled_attention_28_amd import binding  # noqa: E402
@@ -106,6 +109,7 @@ class Step:
         self.code = binding.FA_DTYPE_BF16 if w.dtype == "bf16" else binding.FA_DTYPE_F32
         self.stream = torch.cuda.current_stream()
         self.sh = self.stream.cuda_stream
+        self.precision = binding.FA_PRECISION_BF16
 
     def fwd(self):
         w = self.w
@@ -125,7 +129,7 @@ class Step:
                             self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
                             self.dv.data_ptr(), self.ws.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen,
                             w.seqlen, w.head_dim, w.scale, int(w.causal), self.code, self.code, self.code,
-                            self.sh)
+                            self.precision, self.sh)
         if rc:
             raise binding.FAError(rc, fn.__name__, binding.fa_last_error())
 
@@ -194,7 +198,8 @@ def bench_varlen(args):
     def bwd():
         rc = binding.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
-                                   cu.data_ptr(), cu.data_ptr(), B, mx, mx, T, T, H, H, d, scale, 1, bf, bf, bf, sh)
+                                   cu.data_ptr(), cu.data_ptr(), B, mx, mx, T, T, H, H, d, scale, 1, bf, bf, bf,
+                                   binding.FA_PRECISION_BF16, sh)
         if rc:
             raise binding.FAError(rc, "fa_bwd_varlen", binding.fa_last_error())
 
@@ -252,7 +257,8 @@ def bench_sweep(args):
                     def bwd():
                         rc = binding.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
-                                            B, Hq, Hkv, n, n, d, scale, int(causal), bf, bf, bf, sh)
+                                            B, Hq, Hkv, n, n, d, scale, int(causal), bf, bf, bf,
+                                            binding.FA_PRECISION_BF16, sh)
                         if rc:
                             raise binding.FAError(rc, "fa_bwd", binding.fa_last_error())
 
@@ -384,19 +390,25 @@ def _template_args(kernel):
     return [t.strip() for t in kernel[kernel.index("<") + 1:kernel.rindex(">(")].split(",")]
 
 
+# Position of the VARLEN / PERSIST template argument of each kernel template
+# (fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>,
+# bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN>, bwd_dq_kernel<D, CAUSAL, VARLEN, NW>).
+_VARLEN_ARG = {
+    "void fa::fwd_kernel<": 5,
+    "void fa::bwd_dkdv_kernel<": 3,
+    "void fa::bwd_dq_kernel<": 2,
+}
+_PERSIST_ARG = {"void fa::fwd_kernel<": 6}
+
+
 def _call_of(kernel):
     t = _template_args(kernel)
-    # fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>: the
-    # variable-length and persistent instances set VARLEN / PERSIST
-    if kernel.startswith("void fa::fwd_kernel<") and len(t) >= 6:
-        if t[5] == "true":
-            return "fa_fwd_varlen"
-        if len(t) >= 7 and t[6] == "true":
+    for prefix, pos in _PERSIST_ARG.items():
+        if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
             return "fa_fwd_persistent"
-    if ((kernel.startswith("void fa::bwd_dkdv_kernel<") and len(t) == 4)
-            or (kernel.startswith("void fa::bwd_dq_kernel<") and len(t) == 3)):
-        if t[-1] == "true":
-            return "fa_bwd_varlen"
+    for prefix, pos in _VARLEN_ARG.items():
+        if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
+            return "fa_fwd_varlen" if prefix == "void fa::fwd_kernel<" else "fa_bwd_varlen"
     if "bwd_preprocess_kernel" in kernel:
         zero_dq = kernel.rstrip().endswith(", true>(fa::BwdArgs)") or "Lb1EEEv" in kernel or ", true>" in kernel
         return "fa_bwd_atomic" if zero_dq else "fa_bwd"
@@ -411,7 +423,7 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
     two counter runs (prof_dir/fetch: FETCH_SIZE, prof_dir/write: WRITE_SIZE,
     each with --copy-calibration calib_mib) into markdown tables, and record
     the copy-calibrated HBM bytes per launch of fa_fwd / fa_bwd for the
-    current kernel sources in measured_traffic.json."""
+    current kernel sources in TRAFFIC_JSON."""
     import csv
     import glob
 
@@ -485,7 +497,7 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
            "kernel_sources_sha256": csrc_sha256(), "workload": "fwd_bf16_causal_b8_h16_n2048_d128",
            "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4)}
     rec.update({k: v for k, v in per_call.items() if k in ("fa_fwd", "fa_bwd")})
-    out_path = out_path or os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
+    out_path = out_path or TRAFFIC_JSON
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(f"\nkernel sources sha256 {rec['kernel_sources_sha256']}")
@@ -534,7 +546,7 @@ def measured_traffic(call):
     """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
     have changed since they were taken."""
-    rec_path = os.path.join(ROOT, "exact_tiled_attention_28_amd", "measured_traffic.json")
+    rec_path = TRAFFIC_JSON
     if not os.path.exists(rec_path):
         return None
     with open(rec_path) as fh:

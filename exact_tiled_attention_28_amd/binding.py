@@ -29,6 +29,8 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_PRECISION_BF16 = 0
+FA_PRECISION_HILO = 1
 
 _lib = None
 
@@ -58,7 +60,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [_c_ptr] * 5 + [_c_int] * 6 + [_c_float] + [_c_int] * 3 + [_c_ptr]
     for fn in (lib.fa_bwd, lib.fa_bwd_atomic):
         fn.restype = _c_int
-        fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+        fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 5 + [_c_ptr]
     # (looked up only if present, so that an older build still loads for the
     # fixed-length calls; calling a missing function raises AttributeError)
     if hasattr(lib, "fa_fwd_varlen"):
@@ -66,7 +68,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.fa_fwd_varlen.argtypes = [_c_ptr] * 7 + [_c_int] * 8 + [_c_float] + [_c_int] * 3 + [_c_ptr]
     if hasattr(lib, "fa_bwd_varlen"):
         lib.fa_bwd_varlen.restype = _c_int
-        lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 4 + [_c_ptr]
+        lib.fa_bwd_varlen.argtypes = [_c_ptr] * 12 + [_c_int] * 8 + [_c_float] + [_c_int] * 5 + [_c_ptr]
     if hasattr(lib, "fa_fwd_persistent"):
         lib.fa_fwd_persistent.restype = _c_int
         lib.fa_fwd_persistent.argtypes = [_c_ptr] * 6 + [_c_int] * 6 + [_c_float] + [_c_int] * 3 + [_c_ptr]
@@ -102,17 +104,17 @@ def fa_fwd(q, k, v, o, lse, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, he
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
-           head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream) -> int:
+           head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream) -> int:
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
                                  seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
-                                 stream)
+                                 precision, stream)
 
 
 def fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
-                  head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream) -> int:
+                  head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream) -> int:
     return load_library().fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
                                         seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
-                                        stream)
+                                        precision, stream)
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads,
@@ -124,10 +126,10 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k
 
 def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k,
                   total_q, total_k, n_q_heads, n_kv_heads, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
-                  stream) -> int:
+                  precision, stream) -> int:
     return load_library().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_q, cu_k, batch,
                                         max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim,
-                                        scale, causal, in_dtype, o_dtype, grad_dtype, stream)
+                                        scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream)
 
 
 def fa_fwd_persistent(q, k, v, o, lse, sched, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim, scale,
@@ -222,10 +224,10 @@ def forward(q, k, v, scale, causal, out_dtype=None, o=None, lse=None, stream=Non
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None, atomic_dq=False):
+def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None, atomic_dq=False, hilo=False):
     """dQ (fp32), dK, dV (grad_dtype, default the input dtype) and the
     workspace holding D. Returns (dq, dk, dv, dvec). atomic_dq selects
-    fa_bwd_atomic instead of fa_bwd."""
+    fa_bwd_atomic instead of fa_bwd; hilo selects FA_PRECISION_HILO."""
     import torch
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -240,7 +242,8 @@ def backward(q, k, v, o, lse, do, scale, causal, grad_dtype=None, stream=None, a
     fn = fa_bwd_atomic if atomic_dq else fa_bwd
     rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
-            int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
+            int(bool(causal)), _dtype_code(q), _dtype_code(o), gc,
+            FA_PRECISION_HILO if hilo else FA_PRECISION_BF16, _stream_handle(stream))
     _check(rc, fn.__name__)
     return dq, dk, dv, ws[:B * Hq * Nq].view(B, Hq, Nq)
 
@@ -269,9 +272,10 @@ def forward_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, max_seqlen_k, scale, causa
 
 
 def backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_seqlen_q, max_seqlen_k, scale, causal, grad_dtype=None,
-                    stream=None):
-    """Packed variable-length backward (layouts as in forward_varlen).
-    Returns (dq fp32 [Hq, total_q, d], dk, dv [Hkv, total_k, d], D [Hq, total_q])."""
+                    stream=None, hilo=False):
+    """Packed variable-length backward (layouts as in forward_varlen; hilo
+    selects FA_PRECISION_HILO). Returns (dq fp32 [Hq, total_q, d], dk, dv
+    [Hkv, total_k, d], D [Hq, total_q])."""
     import torch
     Hq, total_q, d = q.shape
     Hkv, total_k = k.shape[0], k.shape[1]
@@ -286,7 +290,8 @@ def backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_seqlen_q, max_seqlen_k,
     rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(),
                        cu_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, d,
-                       float(scale), int(bool(causal)), _dtype_code(q), _dtype_code(o), gc, _stream_handle(stream))
+                       float(scale), int(bool(causal)), _dtype_code(q), _dtype_code(o), gc,
+                       FA_PRECISION_HILO if hilo else FA_PRECISION_BF16, _stream_handle(stream))
     _check(rc, "fa_bwd_varlen")
     return dq, dk, dv, ws[:Hq * total_q].view(Hq, total_q)
 

@@ -97,12 +97,14 @@ size_t fa_fwd_persistent_sched_bytes(void) { return 9 * sizeof(int); }
 static int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads,
                       int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
-                      int in_dtype, int o_dtype, int grad_dtype, void* stream, bool atomic_dq, const char* name) {
+                      int in_dtype, int o_dtype, int grad_dtype, int precision, void* stream, bool atomic_dq,
+                      const char* name) {
   std::string err;
   const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
   if (int rc = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, s, scale, causal, in_dtype, o_dtype,
                              grad_dtype, err))
     return fail(rc, err);
+  if (int rc = fa::check_precision(precision, atomic_dq, err)) return fail(rc, err);
   fa::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -123,7 +125,7 @@ static int bwd_common(const void* q, const void* k, const void* v, const void* o
   a.scale = scale;
   a.c = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_bwd(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
-                                atomic_dq, (hipStream_t)stream);
+                                atomic_dq, precision == FA_PRECISION_HILO, (hipStream_t)stream);
   return hip_status(e, name);
 }
 
@@ -132,17 +134,19 @@ extern "C" {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
            int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
-           void* stream) {
+           int precision, void* stream) {
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
-                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream, false, "fa_bwd launch");
+                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream, false,
+                    "fa_bwd launch");
 }
 
 int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   float* dq, void* dk, void* dv, float* workspace, int batch, int n_q_heads, int n_kv_heads,
                   int seqlen_q, int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype,
-                  int grad_dtype, void* stream) {
+                  int grad_dtype, int precision, void* stream) {
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
-                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, stream, true, "fa_bwd_atomic launch");
+                    head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream, true,
+                    "fa_bwd_atomic launch");
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
@@ -186,7 +190,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   float* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int n_q_heads,
                   int n_kv_heads, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
-                  void* stream) {
+                  int precision, void* stream) {
   std::string err;
   int rc;
   if ((rc = fa::check_ptr(q, "q", err)) || (rc = fa::check_ptr(k, "k", err)) || (rc = fa::check_ptr(v, "v", err)) ||
@@ -200,6 +204,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   const fa::VarlenShape s{batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim};
   if ((rc = fa::check_varlen(cu_seqlens_q, cu_seqlens_k, s, scale, causal, err))) return fail(rc, err);
   if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "the backward pass takes bf16 q, k, v, dout");
+  if ((rc = fa::check_precision(precision, false, err))) return fail(rc, err);
   fa::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -224,7 +229,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   a.total_q = total_q;
   a.total_k = total_k;
   hipError_t e = fa::launch_bwd_varlen(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32,
-                                       (hipStream_t)stream);
+                                       precision == FA_PRECISION_HILO, (hipStream_t)stream);
   return hip_status(e, "fa_bwd_varlen launch");
 }
 
@@ -305,6 +310,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 1; }
+int fa_version(void) { return 2; }
 
 }  // extern "C"

@@ -111,6 +111,20 @@ inline int check_bwd(const void* q, const void* k, const void* v, const void* o,
   return FA_OK;
 }
 
+// The backward's precision argument (enum fa_precision); the atomic scheme
+// takes FA_PRECISION_BF16 only.
+inline int check_precision(int precision, bool atomic_dq, std::string& err) {
+  if (precision != FA_PRECISION_BF16 && precision != FA_PRECISION_HILO) {
+    err = "precision must be FA_PRECISION_BF16 or FA_PRECISION_HILO";
+    return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (atomic_dq && precision != FA_PRECISION_BF16) {
+    err = "fa_bwd_atomic supports FA_PRECISION_BF16 only";
+    return FA_ERR_UNSUPPORTED;
+  }
+  return FA_OK;
+}
+
 // Packed variable-length batch (fa_fwd_varlen / fa_bwd_varlen).
 struct VarlenShape {
   int batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, head_dim;

@@ -428,23 +428,27 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
 // own 32 query rows and summing the halves at the end, this halves the
 // accumulator registers, which pays for K and V in registers (no K/V operand
 // reads from LDS) and leaves room for the scheduler.
-template <int D>
+template <int D, bool HILO = false>
 struct DkdvTile {
   static constexpr int NW = 8;
   static constexpr int BKV = 128, BQ = 64;
   static constexpr int ROWB = D * 2, RC = ROWB / 16;
   static constexpr int QTILEB = BQ * ROWB;
   static constexpr int QCPW = QTILEB / (1024 * NW);
-  static constexpr int XB = 4 * 64 * 16;  // per wavefront: P and dS, 2 x bf16x8 each per lane
+  // per wavefront: P and dS, 2 x bf16x8 each per lane (and their low halves
+  // when they are carried as bf16 pairs)
+  static constexpr int XB = (HILO ? 8 : 4) * 64 * 16;
   // LDS (static): exchange [NW][XB], Q and dO tiles x 2, L and D x 2
   static constexpr int LDS_BYTES = NW * XB + 4 * QTILEB + 4 * BQ * 4;
   static_assert(QTILEB % (1024 * NW) == 0, "tiles must split evenly");
   static_assert(D % 64 == 0, "each wavefront takes whole 32-wide head-dim blocks of one half");
 };
 
-template <int D, bool CAUSAL, bool GF32, bool VARLEN = false>
+// HILO: P and dS enter the dV and dK products as bf16 pairs hi + lo (two
+// products each, see bf16_residual8) instead of one bf16 rounding.
+template <int D, bool CAUSAL, bool GF32, bool VARLEN = false, bool HILO = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdArgs a) {
-  using T = DkdvTile<D>;
+  using T = DkdvTile<D, HILO>;
   constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB;
   constexpr int QCPW = T::QCPW, XB = T::XB;
   constexpr int NKK = D / 16, NDH = D / 64;  // NDH: 32-wide head-dim blocks per half
@@ -600,8 +604,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const char* const ptX = sX + (w ^ 4) * XB;
 
   // P and dS of this wavefront's 32 x 32 block (keys x its query half).
+  // With HILO, pl and dsl receive the low halves of P and dS.
   auto scores = [&](auto mask_tag, int q0, const char* tQ, const char* tDO, const float* tL, const float* tD,
-                    bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+                    bf16x8 (&pb)[2], bf16x8 (&dsb)[2], bf16x8 (&pl)[2], bf16x8 (&dsl)[2])
+                    __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* qRows = tQ + h * 32 * ROWB;
     const char* oRows = tDO + h * 32 * ROWB;
@@ -650,6 +656,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int v = 0; v < 8; ++v) pv[v] = s[8 * t + v];
         pb[t] = to_bf16x8(pv);
+        if constexpr (HILO) pl[t] = bf16_residual8(pv, pb[t]);
       }
     }
     // dP = dO V^T, dS = P o (dP - D)
@@ -665,12 +672,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     dsb[0] = to_bf16x8(dsv);
     dsb[1] = to_bf16x8(dsv + 8);
+    if constexpr (HILO) {
+      dsl[0] = bf16_residual8(dsv, dsb[0]);
+      dsl[1] = bf16_residual8(dsv + 8, dsb[1]);
+    }
   };
 
   // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of half hh, for
-  // this wavefront's head-dim half.
-  auto grads = [&](int hh, const char* tQ, const char* tDO, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2])
-      __attribute__((always_inline)) {
+  // this wavefront's head-dim half (with HILO, also the products of the low
+  // halves pl, dsl; unused otherwise).
+  auto grads = [&](int hh, const char* tQ, const char* tDO, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2],
+                   const bf16x8 (&pl)[2], const bf16x8 (&dsl)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -679,6 +691,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
         dvacc[db] = mfma_bf16(cat4(lo, hi), pb[t], dvacc[db]);
+        if constexpr (HILO) dvacc[db] = mfma_bf16(cat4(lo, hi), pl[t], dvacc[db]);
       }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -688,7 +701,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
         dkacc[db] = mfma_bf16(cat4(lo, hi), dsb[t], dkacc[db]);
+        if constexpr (HILO) dkacc[db] = mfma_bf16(cat4(lo, hi), dsl[t], dkacc[db]);
       }
+  };
+  // The four (or eight, with HILO) bf16x8 exchange slots of a wavefront:
+  // P hi, dS hi, then P lo, dS lo.
+  auto read_x = [&](const char* X, bf16x8 (&pb)[2], bf16x8 (&dsb)[2], bf16x8 (&pl)[2], bf16x8 (&dsl)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pb[t] = *(const bf16x8*)(X + (t * 64 + lane) * 16);
+      dsb[t] = *(const bf16x8*)(X + ((2 + t) * 64 + lane) * 16);
+      if constexpr (HILO) {
+        pl[t] = *(const bf16x8*)(X + ((4 + t) * 64 + lane) * 16);
+        dsl[t] = *(const bf16x8*)(X + ((6 + t) * 64 + lane) * 16);
+      }
+    }
   };
 
   // One Q block: its tiles in (tQ, tDO, tL, tD), the next block's loads go to
@@ -704,30 +732,37 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool act0 = !CAUSAL || kv0 + 32 * kg <= q0 + 31;
     const bool act1 = !CAUSAL || kv0 + 32 * kg <= q0 + 63;
     const bool mine = h ? act1 : act0;
-    bf16x8 pb[2] = {}, dsb[2] = {};
+    bf16x8 pb[2] = {}, dsb[2] = {}, pl[2] = {}, dsl[2] = {};
     if (mine) {
       const bool need_mask = (CAUSAL && kv0 + 32 * kg + 31 > q0 + 32 * h) || (kv0 + 32 * kg + 32 > Nk);
       if (need_mask)
-        scores(std::true_type{}, q0, tQ, tDO, tL, tD, pb, dsb);
+        scores(std::true_type{}, q0, tQ, tDO, tL, tD, pb, dsb, pl, dsl);
       else
-        scores(std::false_type{}, q0, tQ, tDO, tL, tD, pb, dsb);
-      *(bf16x8*)(myX + (0 * 64 + lane) * 16) = pb[0];
-      *(bf16x8*)(myX + (1 * 64 + lane) * 16) = pb[1];
-      *(bf16x8*)(myX + (2 * 64 + lane) * 16) = dsb[0];
-      *(bf16x8*)(myX + (3 * 64 + lane) * 16) = dsb[1];
+        scores(std::false_type{}, q0, tQ, tDO, tL, tD, pb, dsb, pl, dsl);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        *(bf16x8*)(myX + (t * 64 + lane) * 16) = pb[t];
+        *(bf16x8*)(myX + ((2 + t) * 64 + lane) * 16) = dsb[t];
+        if constexpr (HILO) {
+          *(bf16x8*)(myX + ((4 + t) * 64 + lane) * 16) = pl[t];
+          *(bf16x8*)(myX + ((6 + t) * 64 + lane) * 16) = dsl[t];
+        }
+      }
     }
     // The exchange needs only the P/dS writes to have landed; the Q/dO tiles
     // of the next block stay in flight across this barrier.
     wait_lds();
     lds_barrier();
-    if (mine) grads(h, tQ, tDO, pb, dsb);
+    if (mine) {
+      // With HILO the wavefront's own P and dS are read back from the
+      // exchange rather than kept in registers across the barrier.
+      if constexpr (HILO) read_x(myX, pb, dsb, pl, dsl);
+      grads(h, tQ, tDO, pb, dsb, pl, dsl);
+    }
     if (h ? act0 : act1) {
-      bf16x8 ppb[2], pds[2];
-      ppb[0] = *(const bf16x8*)(ptX + (0 * 64 + lane) * 16);
-      ppb[1] = *(const bf16x8*)(ptX + (1 * 64 + lane) * 16);
-      pds[0] = *(const bf16x8*)(ptX + (2 * 64 + lane) * 16);
-      pds[1] = *(const bf16x8*)(ptX + (3 * 64 + lane) * 16);
-      grads(h ^ 1, tQ, tDO, ppb, pds);
+      bf16x8 ppb[2], pds[2], ppl[2], pdsl[2];
+      read_x(ptX, ppb, pds, ppl, pdsl);
+      grads(h ^ 1, tQ, tDO, ppb, pds, ppl, pdsl);
     }
     if (has_next) store_ld(nL, nD);
     wait_vmem();
@@ -773,7 +808,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 // S^T = K Q^T and dP^T = V dO^T take Q and dO as register B operands, L and D
 // are per-lane scalars, and dQ^T += K^T dS^T takes dS^T straight from the
 // accumulator registers and K^T by transpose reads of the K tile.
-template <int D, bool CAUSAL, bool VARLEN = false, int NW = 4>
+// HILO: dS enters the dQ product as a bf16 pair hi + lo (two products, see
+// bf16_residual8) instead of one bf16 rounding.
+template <int D, bool CAUSAL, bool VARLEN = false, int NW = 4, bool HILO = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdArgs a) {
   constexpr int BR = 32 * NW, BC = 64, NKB = BC / 32;
   constexpr int ROWB = D * 2, RC = ROWB / 16, TILEB = BC * ROWB, CPW = TILEB / (1024 * NW);
@@ -960,6 +997,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
         const bf16x8 sb = to_bf16x8(dsv + 8 * th);
+        bf16x8 sl;
+        if constexpr (HILO) sl = bf16_residual8(dsv + 8 * th, sb);
         const int t = 2 * kb + th;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -967,6 +1006,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
           const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][0]));
           const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(kp + troff[db][1]));
           dqacc[db] = mfma_bf16(cat4(lo, hi), sb, dqacc[db]);
+          if constexpr (HILO) dqacc[db] = mfma_bf16(cat4(lo, hi), sl, dqacc[db]);
         }
       }
       // Keep the next block's operand reads from being hoisted into this one
@@ -1055,10 +1095,10 @@ static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool GF32>
+template <int D, bool CAUSAL, bool GF32, bool HILO>
 static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  using T = DkdvTile<D>;
-  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32>;
+  using T = DkdvTile<D, HILO>;
+  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, false, HILO>;
   const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, stream, a);
   return hipGetLastError();
@@ -1071,17 +1111,18 @@ static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 // 4K; at d = 64 within +-1 % at 16K, so d = 64 keeps 4 wavefronts.
 constexpr int kDq8MinKeys = 8192;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool HILO>
 static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   if constexpr (D == 128) {
     if (a.Nk >= kDq8MinKeys) {
       const long long blocks8 = (long long)a.B * a.Hq * ceil_div(a.Nq, 256);
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, 8>), dim3((unsigned)blocks8), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, 8, HILO>), dim3((unsigned)blocks8), dim3(512), 0, stream,
+                         a);
       return hipGetLastError();
     }
   }
   const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, 4, HILO>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1090,7 +1131,7 @@ static hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 // backward (fa_bwd_atomic) keeps the separate preprocess kernel, which also
 // zeroes its dQ accumulator.
 template <int D, bool CAUSAL, bool GF32>
-static hipError_t launch_bwd_all(const BwdArgs& a0, bool o_f32, bool atomic_dq, hipStream_t s) {
+static hipError_t launch_bwd_all(const BwdArgs& a0, bool o_f32, bool atomic_dq, bool hilo, hipStream_t s) {
   BwdArgs a = a0;
   a.o_f32 = o_f32 ? 1 : 0;
   if (atomic_dq) {
@@ -1106,59 +1147,75 @@ static hipError_t launch_bwd_all(const BwdArgs& a0, bool o_f32, bool atomic_dq, 
     if (e != hipSuccess) return e;
     return launch_bwd_main<D, CAUSAL, GF32, true>(a, s);
   }
-  hipError_t e = launch_bwd_dq<D, CAUSAL>(a, s);
+  if (hilo) {
+    hipError_t e = launch_bwd_dq<D, CAUSAL, true>(a, s);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dkdv<D, CAUSAL, GF32, true>(a, s);
+  }
+  hipError_t e = launch_bwd_dq<D, CAUSAL, false>(a, s);
   if (e != hipSuccess) return e;
-  return launch_bwd_dkdv<D, CAUSAL, GF32>(a, s);
+  return launch_bwd_dkdv<D, CAUSAL, GF32, false>(a, s);
 }
 
 // Packed variable-length batch: the dQ pass (which forms and stores D) and
 // then the dK/dV pass; both grids cover the longest sequence and workgroups
 // past their sequence's end exit at once. Rows of D that belong to no
 // sequence are never read.
-template <int D, bool CAUSAL, bool GF32>
-static hipError_t launch_bwd_varlen_t(const BwdArgs& a0, bool o_f32, hipStream_t s) {
+template <int D, bool CAUSAL, bool GF32, bool HILO>
+static hipError_t launch_bwd_varlen_h(const BwdArgs& a0, bool o_f32, hipStream_t s) {
   BwdArgs a = a0;
   a.o_f32 = o_f32 ? 1 : 0;
   {
     const long long blocks = (long long)a.B * a.Hq * ceil_div(a.Nq, 128);
     if (blocks > 0) {
-      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, 4, HILO>), dim3((unsigned)blocks), dim3(256), 0, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
-  using T = DkdvTile<D>;
-  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true>;
+  using T = DkdvTile<D, HILO>;
+  auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true, HILO>;
   const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
   if (blocks > 0) hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * T::NW), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s) {
+template <int D, bool CAUSAL, bool GF32>
+static hipError_t launch_bwd_varlen_t(const BwdArgs& a, bool o_f32, bool hilo, hipStream_t s) {
+  return hilo ? launch_bwd_varlen_h<D, CAUSAL, GF32, true>(a, o_f32, s)
+              : launch_bwd_varlen_h<D, CAUSAL, GF32, false>(a, o_f32, s);
+}
+
+hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool hilo,
+                             hipStream_t s) {
   if (head_dim == 64) {
     if (causal)
-      return grad_f32 ? launch_bwd_varlen_t<64, true, true>(a, o_f32, s) : launch_bwd_varlen_t<64, true, false>(a, o_f32, s);
-    return grad_f32 ? launch_bwd_varlen_t<64, false, true>(a, o_f32, s) : launch_bwd_varlen_t<64, false, false>(a, o_f32, s);
+      return grad_f32 ? launch_bwd_varlen_t<64, true, true>(a, o_f32, hilo, s)
+                      : launch_bwd_varlen_t<64, true, false>(a, o_f32, hilo, s);
+    return grad_f32 ? launch_bwd_varlen_t<64, false, true>(a, o_f32, hilo, s)
+                    : launch_bwd_varlen_t<64, false, false>(a, o_f32, hilo, s);
   }
   if (causal)
-    return grad_f32 ? launch_bwd_varlen_t<128, true, true>(a, o_f32, s) : launch_bwd_varlen_t<128, true, false>(a, o_f32, s);
-  return grad_f32 ? launch_bwd_varlen_t<128, false, true>(a, o_f32, s) : launch_bwd_varlen_t<128, false, false>(a, o_f32, s);
+    return grad_f32 ? launch_bwd_varlen_t<128, true, true>(a, o_f32, hilo, s)
+                    : launch_bwd_varlen_t<128, true, false>(a, o_f32, hilo, s);
+  return grad_f32 ? launch_bwd_varlen_t<128, false, true>(a, o_f32, hilo, s)
+                  : launch_bwd_varlen_t<128, false, false>(a, o_f32, hilo, s);
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool o_f32, bool grad_f32, bool atomic_dq, bool hilo,
                                hipStream_t s) {
   if (causal)
-    return grad_f32 ? launch_bwd_all<D, true, true>(a, o_f32, atomic_dq, s)
-                    : launch_bwd_all<D, true, false>(a, o_f32, atomic_dq, s);
-  return grad_f32 ? launch_bwd_all<D, false, true>(a, o_f32, atomic_dq, s)
-                  : launch_bwd_all<D, false, false>(a, o_f32, atomic_dq, s);
+    return grad_f32 ? launch_bwd_all<D, true, true>(a, o_f32, atomic_dq, hilo, s)
+                    : launch_bwd_all<D, true, false>(a, o_f32, atomic_dq, hilo, s);
+  return grad_f32 ? launch_bwd_all<D, false, true>(a, o_f32, atomic_dq, hilo, s)
+                  : launch_bwd_all<D, false, false>(a, o_f32, atomic_dq, hilo, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
-                      hipStream_t s) {
-  return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, atomic_dq, s)
-                        : launch_bwd_d<128>(a, causal, o_f32, grad_f32, atomic_dq, s);
+                      bool hilo, hipStream_t s) {
+  return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, atomic_dq, hilo, s)
+                        : launch_bwd_d<128>(a, causal, o_f32, grad_f32, atomic_dq, hilo, s);
 }
 
 }  // namespace fa

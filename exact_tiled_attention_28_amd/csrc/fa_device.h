@@ -63,6 +63,19 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
   return __builtin_convertvector(v, bf16x8);
 }
 
+// Second half of a two-term bf16 representation x = hi + lo: with hi the RNE
+// bf16 rounding of x, x - hi is exact in fp32 (it only holds the low bits of
+// x's significand), and lo is its RNE bf16 rounding, so hi + lo carries x to
+// a relative error of at most 2^-18 (two products, one per term, replace the
+// single bf16 product).
+__device__ __forceinline__ bf16x8 bf16_residual8(const float* x, bf16x8 hi) {
+  const f32x8 h = __builtin_convertvector(hi, f32x8);
+  float r[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) r[v] = x[v] - h[v];
+  return to_bf16x8(r);
+}
+
 // LDS tiles hold rows of ROW_CHUNKS 16-byte chunks (ROW_CHUNKS >= 8, rows a
 // multiple of 128 bytes). Chunk c of row r is stored at chunk position
 // c ^ swz(r). The gfx950 LDS serves 64 banks of 4 bytes (256 bytes) per

@@ -53,13 +53,16 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool in_f32, bool causal, bool out_f32, hipStream_t s);
+// hilo: P and dS enter the gradient products as bf16 pairs hi + lo
+// (FA_PRECISION_HILO); the atomic scheme does not take it.
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool atomic_dq,
-                      hipStream_t s);
+                      bool hilo, hipStream_t s);
 hipError_t launch_fwd_varlen(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
 hipError_t launch_fwd_persistent(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
                                int N, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, bool out_f32, hipStream_t s);
-hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, hipStream_t s);
+hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool hilo,
+                             hipStream_t s);
 
 }  // namespace fa

@@ -8,8 +8,11 @@
  * sections 2.2 and 6.1), K/V tiles streamed through LDS, an unnormalised output
  * rescaled only by exp(m_old - m_new) and divided once at the end (section
  * 3.2), causal tiles above the diagonal skipped (section 5.3), and a backward
- * pass that owns one K/V column block per workgroup and adds dQ atomically
- * (section 7.2; CSDN FlashAttention-2 article, "并行性 / 反向传播").
+ * pass in two launches (section 7.2; CSDN FlashAttention-2 article,
+ * "并行性 / 反向传播"): a Q-outer pass that forms D = rowsum(dO o O) and
+ * writes dQ once, then workgroups that each own one K/V column block and
+ * write dK, dV once; no atomics, deterministic. fa_bwd_atomic is the
+ * single-pass variant that adds dQ with fp32 atomics after a D preprocess.
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory)
@@ -31,8 +34,9 @@
  *    enqueued, and leave every output untouched. A launch failure returns
  *    FA_ERR_HIP. Faults inside a kernel surface at the caller's next
  *    synchronisation, as usual for HIP.
- *  - Numerics: fp32 accumulation; probabilities P and dS are rounded to
- *    bfloat16 (round-to-nearest-even) before the bf16 matrix products; the
+ *  - Numerics: fp32 accumulation; probabilities P (and in the backward dS)
+ *    are rounded to bfloat16 (round-to-nearest-even) before the bf16 matrix
+ *    products, or carried as bf16 pairs (enum fa_precision, backward); the
  *    scale is applied in fp32 to the fp32 scores, never folded into a rounded
  *    operand. NaN or Inf in an input row propagates to the outputs that
  *    depend on it.
@@ -58,6 +62,23 @@ enum fa_status {
 enum fa_dtype {
   FA_DTYPE_F32 = 0,
   FA_DTYPE_BF16 = 1
+};
+
+/* How the backward passes feed the probabilities P and their gradients dS
+ * to the bf16 matrix products dV = P^T dO, dK = dS^T Q, dQ = dS K.
+ *  FA_PRECISION_BF16: each is rounded once to bf16 (round-to-nearest-even),
+ *    the 16-bit products of the pages (CSDN FlashAttention-2 article, the
+ *    FP16/BF16 matrix multiplies): relative error up to 2^-9 per element.
+ *  FA_PRECISION_HILO: each is carried as a pair of bf16 values hi + lo, with
+ *    hi = RNE(x) and lo = RNE(x - hi) (x - hi is exact in fp32), and enters
+ *    two products, one per term: relative error up to 2^-18 per element, at
+ *    the cost of one more product per gradient (7 instead of 5 per score
+ *    pair, 10 instead of 7 in fa_bwd's two passes). For gradients that the
+ *    bf16 rounding would move by more than the caller's tolerance (grouped
+ *    heads summed over many rows, near one-hot probabilities). */
+enum fa_precision {
+  FA_PRECISION_BF16 = 0,
+  FA_PRECISION_HILO = 1
 };
 
 /*
@@ -109,6 +130,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   dk, dv   [B][Hkv][Nk][d] grad_dtype (bf16 or fp32), fully overwritten
  *   workspace  device buffer of at least fa_bwd_workspace_bytes() bytes; on
  *            return it holds D as fp32 [B][Hq][Nq]
+ *   precision  FA_PRECISION_BF16 or FA_PRECISION_HILO (enum fa_precision)
  *   other arguments as in fa_fwd.
  * Returns FA_OK or an fa_status code.
  */
@@ -116,7 +138,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, float* dq, void* dk, void* dv,
            float* workspace, int batch, int n_q_heads, int n_kv_heads,
            int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
-           int in_dtype, int o_dtype, int grad_dtype, void* stream);
+           int in_dtype, int o_dtype, int grad_dtype, int precision,
+           void* stream);
 
 /*
  * fa_bwd_atomic — the same computation, arguments and results as fa_bwd, in
@@ -125,14 +148,15 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * section 7.2; CSDN article, "并行性 / 反向传播"); the preprocess kernel
  * zeroes dq first. Fewer matrix products than fa_bwd, but the atomic traffic
  * is (number of K/V blocks) * seqlen_q * head_dim * 4 bytes per query head,
- * and the last bits of dq depend on the order of the atomic adds.
+ * and the last bits of dq depend on the order of the atomic adds. precision
+ * must be FA_PRECISION_BF16 (FA_ERR_UNSUPPORTED otherwise).
  */
 int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout, float* dq, void* dk,
                   void* dv, float* workspace, int batch, int n_q_heads,
                   int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim,
                   float scale, int causal, int in_dtype, int o_dtype,
-                  int grad_dtype, void* stream);
+                  int grad_dtype, int precision, void* stream);
 
 /*
  * fa_fwd_varlen — fa_fwd on a packed batch of sequences of different lengths
@@ -173,6 +197,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
  * least fa_bwd_workspace_bytes(1, n_q_heads, total_q) bytes, holding D as
  * fp32 [Hq][total_q] on return. dq, dk and dv are fully overwritten (keys of
  * a sequence without queries get dK = dV = 0; queries without keys dQ = 0).
+ * precision as in fa_bwd.
  */
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout, float* dq, void* dk,
@@ -180,7 +205,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                   const int* cu_seqlens_k, int batch, int max_seqlen_q,
                   int max_seqlen_k, int total_q, int total_k, int n_q_heads,
                   int n_kv_heads, int head_dim, float scale, int causal,
-                  int in_dtype, int o_dtype, int grad_dtype, void* stream);
+                  int in_dtype, int o_dtype, int grad_dtype, int precision,
+                  void* stream);
 
 /*
  * fa_quantize_fp8 — the FP8 quantization with incoherent processing of the
@@ -265,7 +291,8 @@ const char* fa_status_string(int status);
 /* Thread-local detail of the last failing call on this thread ("" if none). */
 const char* fa_last_error(void);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 2 (2 added the precision argument of the
+ * backward entry points). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -50,14 +50,14 @@ def test_library_exports_every_declared_function(lib):
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "fa.h"\nint main(void) { return fa_version() == 1 ? 0 : 1; }\n')
+    src.write_text('#include "fa.h"\nint main(void) { return fa_version() == 2 ? 0 : 1; }\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", f"-I{os.path.join(ROOT, 'include')}",
                         str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
 
 def test_misc_entry_points(lib):
-    assert binding.fa_version() == 1
+    assert binding.fa_version() == 2
     assert binding.fa_status_string(0) == "FA_OK"
     assert binding.fa_status_string(1) == "FA_ERR_INVALID_ARGUMENT"
     assert binding.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
@@ -84,7 +84,7 @@ def fwd(**kw):
 def bwd(**kw):
     args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, batch=1, n_q_heads=2, n_kv_heads=1,
                 seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
-                stream=None)
+                precision=0, stream=None)
     args.update(kw)
     return binding.fa_bwd(*args.values())
 
@@ -123,16 +123,26 @@ def test_fwd_argument_errors(lib, kw, code, text):
     (dict(in_dtype=0), UNSUP, "bf16"),
     (dict(head_dim=32), UNSUP, "head_dim 32"),
     (dict(causal=1, seqlen_k=15), UNSUP, "seqlen_q == seqlen_k"),
+    (dict(precision=2), INVALID, "FA_PRECISION"),
+    (dict(precision=-1), INVALID, "FA_PRECISION"),
 ])
 def test_bwd_argument_errors(lib, kw, code, text):
     assert bwd(**kw) == code
     assert text in binding.fa_last_error()
     args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, batch=1, n_q_heads=2, n_kv_heads=1,
                 seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
-                stream=None)
+                precision=0, stream=None)
     args.update(kw)
     assert binding.fa_bwd_atomic(*args.values()) == code
     assert text in binding.fa_last_error()
+
+
+def test_bwd_atomic_rejects_hilo(lib):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, batch=1, n_q_heads=2, n_kv_heads=1,
+                seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
+                precision=binding.FA_PRECISION_HILO, stream=None)
+    assert binding.fa_bwd_atomic(*args.values()) == UNSUP
+    assert "FA_PRECISION_BF16 only" in binding.fa_last_error()
 
 
 CU = 0x20000       # fake 4-byte-aligned offset arrays
@@ -150,7 +160,7 @@ def fwd_varlen(**kw):
 def bwd_varlen(**kw):
     args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, cu_q=CU, cu_k=CU, batch=2, max_q=16,
                 max_k=16, total_q=20, total_k=20, n_q_heads=2, n_kv_heads=1, head_dim=64, scale=0.125, causal=0,
-                in_dtype=1, o_dtype=1, grad_dtype=1, stream=None)
+                in_dtype=1, o_dtype=1, grad_dtype=1, precision=0, stream=None)
     if "out_dtype" in kw:
         kw = dict(kw)
         kw["grad_dtype"] = kw.pop("out_dtype")

@@ -45,6 +45,14 @@ def test_kernel_to_entry_point():
     assert bench._call_of("void fa::bwd_dkdv_kernel<128, true, false, true>(fa::BwdArgs)") == "fa_bwd_varlen"
     assert bench._call_of("void fa::bwd_dq_kernel<128, true, true>(fa::BwdArgs)") == "fa_bwd_varlen"
     assert bench._call_of("void fa::bwd_dq_kernel<128, true, false, 4>(fa::BwdArgs)") == "fa_bwd"
+    # the names rocprofv3 prints for the current instances (every template
+    # argument written out)
+    assert bench._call_of("void fa::bwd_dq_kernel<128, true, true, 4>(fa::BwdArgs)") == "fa_bwd_varlen"
+    assert bench._call_of("void fa::bwd_dq_kernel<128, false, false, 8>(fa::BwdArgs)") == "fa_bwd"
+    assert bench._call_of("void fa::bwd_dq_kernel<128, true, false, 8>(fa::BwdArgs)") == "fa_bwd"
+    assert bench._call_of("void fa::bwd_dkdv_kernel<128, true, false, false>(fa::BwdArgs)") == "fa_bwd"
+    assert bench._call_of("void fa::bwd_dkdv_kernel<64, false, true, true>(fa::BwdArgs)") == "fa_bwd_varlen"
+    assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 8, false, false>(fa::FwdArgs)") == "fa_fwd"
     assert bench._call_of("void fa::quantize_fp8_kernel<128>(__bf16 const*, unsigned char*, float*, "
                           "signed char const*, int, int)") == "fa_quantize_fp8"
     assert bench._call_of("void fa::fwd_fp8_kernel<true, false>(fa::FwdArgs)") == "fa_fwd_fp8"

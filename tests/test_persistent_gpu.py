@@ -1,6 +1,6 @@
 """The persistent work-queue forward (fa_fwd_persistent through the C ABI):
 the same per-item arithmetic as fa_fwd's 4-wavefront kernel, so for keys
-below the length where fa_fwd switches to its two-group kernel the outputs
+below the length where fa_fwd switches to its 8-wavefront kernel the outputs
 must be bit-identical to fa_fwd's; everywhere they must meet the forward's
 bounds against the fp64 oracle (O max-abs 1e-2, L 1e-3, O requested in
 fp32). The counter array must be back to zero after every call, including
@@ -72,8 +72,8 @@ def test_persistent_calls_in_a_row_and_bf16_output():
 
 
 def test_persistent_long_keys_against_oracle():
-    # keys >= 4096: fa_fwd uses its two-group kernel, the persistent path the
-    # 4-wavefront one; both within the bounds, on sampled rows
+    # a longer key range than the bit-identity cases; both paths within the
+    # bounds, on sampled rows
     import torch
     B, H, N, d = 1, 2, 4160, 128
     announce(f"fa_fwd_persistent long keys B{B} H{H} N{N}")

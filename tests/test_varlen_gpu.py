@@ -3,10 +3,12 @@
 same seeded inputs.
 
 Bounds as for the fixed-length shapes: O max-abs 1e-2 and L 1e-3 (fp32
-outputs); dQ, dK, dV 1e-2 plus the worst-case effect of rounding P and dS to
-bf16 before the gradient products (test_bwd_gpu.py derives it), computed per
-sequence from the oracle's P. Rows of a sequence without keys must be exactly
-O = 0, L = -inf, dQ = 0; keys of a sequence without queries dK = dV = 0.
+outputs); dQ, dK, dV max-abs 1e-2. The backward runs with FA_PRECISION_HILO
+(P and dS as bf16 pairs) on every case and also with FA_PRECISION_BF16 where
+no query heads are summed into one K/V head (with a group, the bf16 rounding
+of P alone can reach the flat bound on short causal rows; test_bwd_gpu.py).
+Rows of a sequence without keys must be exactly O = 0, L = -inf, dQ = 0; keys
+of a sequence without queries dK = dV = 0.
 """
 
 import numpy as np
@@ -19,8 +21,6 @@ from tests.gpu_util import announce, host
 
 pytestmark = pytest.mark.gpu
 
-U_BF16 = 2.0 ** -9
-
 
 def upload(x):
     import torch
@@ -30,27 +30,6 @@ def upload(x):
 def cu_dev(cu):
     import torch
     return torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
-
-
-def rounding_bounds(inp, scale, causal):
-    """|err| <= 2^-9 sum |P||dO| (dV), 2^-9 s sum |dS||Q| (dK), 2^-9 s sum |dS||K| (dQ)."""
-    q, k, v, do = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do))
-    Hq, Hkv = q.shape[0], k.shape[0]
-    G = Hq // Hkv
-    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    for b in range(inp.cu_q.size - 1):
-        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
-        if q1 == q0 or k1 == k0:
-            continue
-        for h in range(Hq):
-            g = h // G
-            P = oracle.probabilities_head(q[h, q0:q1], k[g, k0:k1], scale, causal)
-            O = P @ v[g, k0:k1]
-            dS = P * (do[h, q0:q1] @ v[g, k0:k1].T - oracle.row_dot(do[h, q0:q1], O)[:, None])
-            bv[g, k0:k1] += np.abs(P).T @ np.abs(do[h, q0:q1])
-            bk[g, k0:k1] += abs(scale) * np.abs(dS).T @ np.abs(q[h, q0:q1])
-            bq[h, q0:q1] = abs(scale) * np.abs(dS) @ np.abs(k[g, k0:k1])
-    return U_BF16 * bq, U_BF16 * bk, U_BF16 * bv
 
 
 CASES = [
@@ -64,7 +43,7 @@ CASES = [
 IDS = [f"{'c' if c[5] else 'n'}d{c[4]}Hq{c[2]}Hkv{c[3]}b{len(c[0])}" for c in CASES]
 
 
-def _run(case, seed, with_bwd):
+def _run(case, seed, with_bwd, hilo=False):
     import torch
     lq, lk, Hq, Hkv, d, causal = case
     lk = lq if lk is None else lk
@@ -78,7 +57,7 @@ def _run(case, seed, with_bwd):
     if with_bwd:
         do = upload(inp.do)
         dq, dk, dv, _ = binding.backward_varlen(q, k, v, o, lse, do, cq, ck, inp.max_q, inp.max_k, scale, causal,
-                                                grad_dtype=torch.float32)
+                                                grad_dtype=torch.float32, hilo=hilo)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return inp, scale, {n: host(t) for n, t in out.items()}
@@ -103,15 +82,18 @@ def test_varlen_forward_parity(case):
     assert np.max(np.abs(r["lse"][:, ~empty] - Lr[:, ~empty]), initial=0) <= 1e-3
 
 
-@pytest.mark.parametrize("case", CASES[:4], ids=IDS[:4])
-def test_varlen_backward_parity(case):
-    announce(f"bwd varlen {case}")
-    inp, scale, r = _run(case, 950 + len(case[0]), True)
+BWD_PARAMS = [(i, hilo) for i, c in enumerate(CASES) for hilo in (False, True) if hilo or c[2] == c[3]]
+
+
+@pytest.mark.parametrize("ci,hilo", BWD_PARAMS, ids=[f"{IDS[i]}-{'hilo' if h else 'bf16'}" for i, h in BWD_PARAMS])
+def test_varlen_backward_parity(ci, hilo):
+    case = CASES[ci]
+    announce(f"bwd varlen {case} hilo={hilo}")
+    inp, scale, r = _run(case, 950 + len(case[0]), True, hilo=hilo)
     dQ, dK, dV = oracle.backward_varlen(inp.q, inp.k, inp.v, inp.do, inp.cu_q, inp.cu_k, scale, case[5])
-    bq, bk, bv = rounding_bounds(inp, scale, case[5])
-    assert np.all(np.abs(r["dq"] - dQ) <= 1e-2 + bq)
-    assert np.all(np.abs(r["dk"] - dK) <= 1e-2 + bk)
-    assert np.all(np.abs(r["dv"] - dV) <= 1e-2 + bv)
+    e = [np.max(np.abs(r["dq"] - dQ)), np.max(np.abs(r["dk"] - dK)), np.max(np.abs(r["dv"] - dV))]
+    print(f"varlen {IDS[ci]} hilo={hilo}: max|d dQ|={e[0]:.3e} max|d dK|={e[1]:.3e} max|d dV|={e[2]:.3e}")
+    assert max(e) <= 1e-2
     # exact zeros where there is nothing to attend to
     assert np.all(r["dq"][:, _no_key_rows(inp)] == 0)
     for b in range(inp.cu_q.size - 1):

@@ -9,6 +9,8 @@ checked against 1e-2 plus half a bf16 ulp of the exact value); O within 1e-5
 for the fp32 workload.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -75,42 +77,107 @@ def test_workload_fwd_bf16(name, full, rows):
     assert worst_o <= 1e-2 and worst_l <= 1e-3
 
 
-@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic"])
-def test_workload_bwd_bf16_causal_b4_h16_n4096_d128(atomic_dq):
+_C5_ORACLE = {}
+
+
+def _c5_oracle(w, inp):
+    """The oracle's gradients of every (batch, head) of the backward workload,
+    computed once per session (about 0.5 s per head)."""
+    if "grads" not in _C5_ORACLE:
+        B, H = w.batch, w.n_q_heads
+        dQ = np.empty((B, H, w.seqlen, w.head_dim))
+        dK = np.empty_like(dQ)
+        dV = np.empty_like(dQ)
+        for b in range(B):
+            for h in range(H):
+                dQ[b, h], dK[b, h], dV[b, h] = oracle.backward_head(inp.q[b, h], inp.k[b, h], inp.v[b, h],
+                                                                     inp.do[b, h], w.scale, w.causal)
+        _C5_ORACLE["grads"] = (dQ, dK, dV)
+    return _C5_ORACLE["grads"]
+
+
+@pytest.mark.parametrize("scheme", ["bf16", "hilo", "atomic"])
+def test_workload_bwd_bf16_causal_b4_h16_n4096_d128(scheme):
+    """The backward workload at full size in the configuration bench times
+    (scheme bf16: fa_bwd, FA_PRECISION_BF16), and with the hi/lo products and
+    the atomic scheme: every one of the 64 heads element by element against
+    the oracle, flat max-abs 1e-2 on dQ, dK, dV (fp32 outputs; bf16 dK, dV
+    within 1e-2 plus half a bf16 ulp)."""
     import torch
     w = WORKLOADS["bwd_bf16_causal_b4_h16_n4096_d128"]
-    announce(f"{w.name} atomic_dq={atomic_dq}")
+    announce(f"{w.name} scheme={scheme}")
     inp = _inputs(w)
     q, k, v, do = upload(inp)
     o, lse = binding.forward(q, k, v, w.scale, w.causal, out_dtype=torch.float32)
-    dq, dk, dv, dvec = binding.backward(q, k, v, o, lse, do, w.scale, w.causal, grad_dtype=torch.float32,
-                                        atomic_dq=atomic_dq)
-    dq2, dk16, dv16, _ = binding.backward(q, k, v, o, lse, do, w.scale, w.causal, grad_dtype=torch.bfloat16,
-                                          atomic_dq=atomic_dq)
+    kw = dict(atomic_dq=scheme == "atomic", hilo=scheme == "hilo")
+    dq, dk, dv, dvec = binding.backward(q, k, v, o, lse, do, w.scale, w.causal, grad_dtype=torch.float32, **kw)
+    dq2, dk16, dv16, _ = binding.backward(q, k, v, o, lse, do, w.scale, w.causal, grad_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
     dQ, dK, dV, dQ2 = host(dq), host(dk), host(dv), host(dq2)
     dK16, dV16 = host(dk16), host(dv16)
     # Atomic accumulation order may differ between runs (only the last bits);
     # the two-pass scheme is bitwise repeatable.
-    if atomic_dq:
+    if scheme == "atomic":
         assert np.max(np.abs(dQ - dQ2)) <= 1e-5
     else:
         assert np.array_equal(dQ, dQ2)
-    rng = np.random.default_rng(99)
-    heads = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
-    worst = [0.0, 0.0, 0.0]
-    for b, h in [tuple(x) for x in rng.permutation(heads)[:2].tolist()]:
-        dq_r, dk_r, dv_r = oracle.backward_head(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], w.scale, True)
-        worst[0] = max(worst[0], np.max(np.abs(dQ[b, h] - dq_r)))
-        worst[1] = max(worst[1], np.max(np.abs(dK[b, h] - dk_r)))
-        worst[2] = max(worst[2], np.max(np.abs(dV[b, h] - dv_r)))
-        assert np.all(np.abs(dK16[b, h] - dk_r) <= 1e-2 + bf16_half_ulp(dk_r))
-        assert np.all(np.abs(dV16[b, h] - dv_r) <= 1e-2 + bf16_half_ulp(dv_r))
-    print(f"{w.name}: max|d dQ|={worst[0]:.3e} max|d dK|={worst[1]:.3e} max|d dV|={worst[2]:.3e}")
-    assert max(worst) <= 1e-2
-    # Sum rules over every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
-    assert np.max(np.abs(dK.sum(axis=2))) <= 0.05
-    ref = inp.do.astype(np.float64).sum(axis=2)
-    assert np.max(np.abs(dV.sum(axis=2) - ref)) <= 0.05 + 1e-4 * np.max(np.abs(ref))
+    dQr, dKr, dVr = _c5_oracle(w, inp)
+    errs = [np.max(np.abs(dQ - dQr)), np.max(np.abs(dK - dKr)), np.max(np.abs(dV - dVr))]
+    per_head = np.max(np.abs(dV - dVr), axis=(2, 3))
+    print(f"{w.name} {scheme}: all 64 heads max|d dQ|={errs[0]:.3e} max|d dK|={errs[1]:.3e} "
+          f"max|d dV|={errs[2]:.3e} (dV per-head median {np.median(per_head):.3e})")
+    assert max(errs) <= 1e-2
+    assert np.all(np.abs(dK16 - dKr) <= 1e-2 + bf16_half_ulp(dKr))
+    assert np.all(np.abs(dV16 - dVr) <= 1e-2 + bf16_half_ulp(dVr))
     # D = rowsum(dO o O) on every row.
     assert np.max(np.abs(host(dvec) - oracle.row_dot(inp.do, host(o)))) <= 1e-3
+
+
+def test_gqa_outlier_bwd_b4_hq32_hkv8_n4096_d128_group():
+    """The GQA outlier shape (B4 Hq32 Hkv8 N4096 d128 causal, 2 of 128
+    channels of Q and K x20, dO drawn after V) through the backward at full
+    size, with FA_PRECISION_HILO: one whole K/V group (4 query heads)
+    element by element against the oracle's gradients, dK and dV summed over
+    the group (CSDN FlashAttention-2 article, "多查询注意力和分组查询注意力"),
+    flat max-abs 1e-2. The gradients here reach a few hundred (the outlier
+    channels enter dK through Q and dQ through K), so the bound is a relative
+    accuracy of about 4e-5: the group's O and L are the oracle's, so that the
+    check measures the backward's own arithmetic (the forward's fp32 O is
+    within its 1e-2 bound, but through D = rowsum(dO o O) and the x20
+    channels of Q an O error of a few 1e-3 moves dK by far more). The bf16
+    scheme and the forward's own O are reported for comparison."""
+    import torch
+    B, Hq, Hkv, N, d = 4, 32, 8, 4096, 128
+    G = Hq // Hkv
+    b, g = 2, 5
+    announce(f"gqa outlier bwd B{B} Hq{Hq} Hkv{Hkv} N{N} group (b={b}, kv head {g})")
+    inp = gen(4, B, Hq, Hkv, N, N, d, with_do=True, outliers=2)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    heads = list(range(g * G, (g + 1) * G))
+    o_ref = np.empty((G, N, d))
+    l_ref = np.empty((G, N))
+    dQr = np.empty((G, N, d))
+    dKr = np.zeros((N, d))
+    dVr = np.zeros((N, d))
+    for t, h in enumerate(heads):
+        o_ref[t], l_ref[t] = oracle.forward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], scale, True)
+        dq_h, dk_h, dv_h = oracle.backward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], inp.do[b, h], scale, True)
+        dQr[t] = dq_h
+        dKr += dk_h
+        dVr += dv_h
+    q, k, v, do = upload(inp)
+    o, lse = binding.forward(q, k, v, scale, True, out_dtype=torch.float32)
+    o_gpu = o.clone()
+    lse_gpu = lse.clone()
+    o[b, heads[0]:heads[-1] + 1] = torch.from_numpy(o_ref.astype(np.float32)).cuda()
+    lse[b, heads[0]:heads[-1] + 1] = torch.from_numpy(l_ref.astype(np.float32)).cuda()
+    res = {}
+    for name, oo, ll, hilo in (("hilo", o, lse, True), ("bf16", o, lse, False), ("hilo, forward's O and L", o_gpu,
+                                                                                 lse_gpu, True)):
+        dq, dk, dv, _ = binding.backward(q, k, v, oo, ll, do, scale, True, grad_dtype=torch.float32, hilo=hilo)
+        torch.cuda.synchronize()
+        res[name] = (np.max(np.abs(host(dq[b, heads[0]:heads[-1] + 1]) - dQr)),
+                     np.max(np.abs(host(dk[b, g]) - dKr)), np.max(np.abs(host(dv[b, g]) - dVr)))
+        print(f"GQA outlier group, {name}: max|d dQ|={res[name][0]:.3e} max|d dK|={res[name][1]:.3e} "
+              f"max|d dV|={res[name][2]:.3e} (max|dK|={np.max(np.abs(dKr)):.1f} max|dV|={np.max(np.abs(dVr)):.1f})")
+    assert max(res["hilo"]) <= 1e-2
