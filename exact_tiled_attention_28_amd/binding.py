@@ -3,7 +3,7 @@ every step of the attention computation runs in the library's HIP kernels.
 
 Two levels:
 
-* ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_atomic`` / ``fa_fwd_varlen`` /
+* ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_atomic`` / ``fa_bwd_noalloc`` / ``fa_fwd_varlen`` /
   ``fa_bwd_varlen`` / ``fa_bwd_workspace_bytes`` / ``fa_status_string`` /
   ``fa_last_error`` / ``fa_version`` mirror the C functions one to one
   (pointers and streams as Python ints);
@@ -61,6 +61,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for fn in (lib.fa_bwd, lib.fa_bwd_atomic):
         fn.restype = _c_int
         fn.argtypes = [_c_ptr] * 10 + [_c_int] * 6 + [_c_float] + [_c_int] * 5 + [_c_ptr]
+    if hasattr(lib, "fa_bwd_noalloc"):
+        lib.fa_bwd_noalloc.restype = _c_int
+        lib.fa_bwd_noalloc.argtypes = [_c_ptr] * 9 + [_c_int] * 6 + [_c_float] + [_c_int] * 5 + [_c_ptr]
     # (looked up only if present, so that an older build still loads for the
     # fixed-length calls; calling a missing function raises AttributeError)
     if hasattr(lib, "fa_fwd_varlen"):
@@ -115,6 +118,13 @@ def fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads
     return load_library().fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads,
                                         seqlen_q, seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype,
                                         precision, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim,
+                   scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream) -> int:
+    return load_library().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, batch, n_q_heads, n_kv_heads, seqlen_q,
+                                         seqlen_k, head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision,
+                                         stream)
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, max_seqlen_q, max_seqlen_k, total_q, total_k, n_q_heads,

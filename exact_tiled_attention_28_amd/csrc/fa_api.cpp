@@ -9,6 +9,8 @@
 #include "fa_args.h"
 #include "fa_launch.h"
 
+static_assert(FA_BWD_NOALLOC_MAX_ROWS == fa::kBwdNoallocMaxRows, "fa.h and the scratch array must agree");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -147,6 +149,48 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, co
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k,
                     head_dim, scale, causal, in_dtype, o_dtype, grad_dtype, precision, stream, true,
                     "fa_bwd_atomic launch");
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   float* dq, void* dk, void* dv, int batch, int n_q_heads, int n_kv_heads, int seqlen_q,
+                   int seqlen_k, int head_dim, float scale, int causal, int in_dtype, int o_dtype, int grad_dtype,
+                   int precision, void* stream) {
+  std::string err;
+  const fa::Shape s{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim};
+  if (int rc = fa::check_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, s, scale, causal, in_dtype, o_dtype,
+                             grad_dtype, err, false))
+    return fail(rc, err);
+  if (int rc = fa::check_precision(precision, false, err)) return fail(rc, err);
+  const long long rows = (long long)batch * n_q_heads * seqlen_q;
+  if (rows > fa::kBwdNoallocMaxRows)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_bwd_noalloc: batch * n_q_heads * seqlen_q = " + std::to_string(rows) +
+                                             " exceeds its scratch of " + std::to_string(fa::kBwdNoallocMaxRows) +
+                                             " rows (FA_BWD_NOALLOC_MAX_ROWS)");
+  float* dvec = nullptr;
+  if (hipError_t e = fa::bwd_noalloc_scratch(&dvec); e != hipSuccess)
+    return hip_status(e, "fa_bwd_noalloc scratch lookup");
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dvec = dvec;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd(a, head_dim, causal != 0, o_dtype == FA_DTYPE_F32, grad_dtype == FA_DTYPE_F32, false,
+                                precision == FA_PRECISION_HILO, (hipStream_t)stream);
+  return hip_status(e, "fa_bwd_noalloc launch");
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,

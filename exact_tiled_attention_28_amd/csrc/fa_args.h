@@ -92,12 +92,16 @@ inline int check_fwd(const void* q, const void* k, const void* v, const void* o,
 
 inline int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                      const float* dq, const void* dk, const void* dv, const float* workspace, const Shape& s,
-                     float scale, int causal, int in_dtype, int o_dtype, int grad_dtype, std::string& err) {
+                     float scale, int causal, int in_dtype, int o_dtype, int grad_dtype, std::string& err,
+                     bool need_workspace = true) {
   int rc;
+  // (workspace == nullptr is accepted only by the caller that passes no
+  // workspace at all, fa_bwd_noalloc, which checks the other pointers here
+  // with need_workspace = false)
   if ((rc = check_ptr(q, "q", err)) || (rc = check_ptr(k, "k", err)) || (rc = check_ptr(v, "v", err)) ||
       (rc = check_ptr(o, "o", err)) || (rc = check_ptr(lse, "lse", err)) || (rc = check_ptr(dout, "dout", err)) ||
       (rc = check_ptr(dq, "dq", err)) || (rc = check_ptr(dk, "dk", err)) || (rc = check_ptr(dv, "dv", err)) ||
-      (rc = check_ptr(workspace, "workspace", err)))
+      (need_workspace && (rc = check_ptr(workspace, "workspace", err))))
     return rc;
   if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !valid_dtype(grad_dtype)) {
     err = "dtypes must be FA_DTYPE_F32 or FA_DTYPE_BF16";

@@ -29,6 +29,7 @@
 // read by transpose reads, then added to HBM with fp32 atomics (lanes cover
 // contiguous head-dim columns, so each atomic instruction touches whole
 // cache lines).
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -1216,6 +1217,42 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, bool o_f32, b
                       bool hilo, hipStream_t s) {
   return head_dim == 64 ? launch_bwd_d<64>(a, causal, o_f32, grad_f32, atomic_dq, hilo, s)
                         : launch_bwd_d<128>(a, causal, o_f32, grad_f32, atomic_dq, hilo, s);
+}
+
+// ---------------------------------------------------------------------------
+// scratch for fa_bwd_noalloc
+// ---------------------------------------------------------------------------
+//
+// D = rowsum(dO o O) of fa_bwd_noalloc lives here instead of in a caller's
+// workspace: a file-scope device array, one copy per device, held until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it only stands in for the symbol); the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and is kept per device. Every fa_bwd_noalloc call on a device shares that
+// device's array: calls that overlap on one device race.
+static __device__ __align__(256) float scratch[kBwdNoallocMaxRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t bwd_noalloc_scratch(float** dvec) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);  // the same address if two threads race here
+  }
+  *dvec = p;
+  return hipSuccess;
 }
 
 }  // namespace fa

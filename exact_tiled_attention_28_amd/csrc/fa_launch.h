@@ -62,6 +62,12 @@ hipError_t launch_fwd_persistent(const FwdArgs& a, int head_dim, bool causal, bo
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
                                int N, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, bool out_f32, hipStream_t s);
+// fa_bwd_noalloc keeps D in a static device array of this many fp32 rows
+// (16 MiB per device); bwd_noalloc_scratch returns its device address on the
+// current device (looked up once per device, with hipGetSymbolAddress).
+constexpr long long kBwdNoallocMaxRows = 1LL << 22;
+hipError_t bwd_noalloc_scratch(float** dvec);
+
 hipError_t launch_bwd_varlen(const BwdArgs& a, int head_dim, bool causal, bool o_f32, bool grad_f32, bool hilo,
                              hipStream_t s);
 

@@ -158,6 +158,32 @@ int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
                   float scale, int causal, int in_dtype, int o_dtype,
                   int grad_dtype, int precision, void* stream);
 
+/* Largest batch * n_q_heads * seqlen_q that fa_bwd_noalloc accepts. */
+#define FA_BWD_NOALLOC_MAX_ROWS 4194304
+
+/*
+ * fa_bwd_noalloc — fa_bwd without the workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). The library keeps D in a static
+ * device array of FA_BWD_NOALLOC_MAX_ROWS fp32 values (16 MiB), one per
+ * device, created with the library's code on that device and held until the
+ * process ends; the call itself allocates nothing. Results are those of
+ * fa_bwd with the same arguments (the same kernels). The caller still
+ * allocates q, k, v, o, lse, dout, dq, dk, dv as for fa_bwd.
+ *   batch * n_q_heads * seqlen_q > FA_BWD_NOALLOC_MAX_ROWS:
+ *            FA_ERR_INVALID_ARGUMENT, before anything is enqueued.
+ *   Every call on a device uses that device's one array: calls that may run
+ *   at the same time on one device (different streams, other host threads)
+ *   race on it and must be serialised by the caller.
+ * Other arguments, ownership and errors as in fa_bwd.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, float* dq, void* dk,
+                   void* dv, int batch, int n_q_heads, int n_kv_heads,
+                   int seqlen_q, int seqlen_k, int head_dim, float scale,
+                   int causal, int in_dtype, int o_dtype, int grad_dtype,
+                   int precision, void* stream);
+
 /*
  * fa_fwd_varlen — fa_fwd on a packed batch of sequences of different lengths
  * (the variable-length batches named on the FlashAttention-3 news page among

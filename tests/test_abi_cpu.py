@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count", "fa_fwd",
+        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count", "fa_fwd",
          "fa_fwd_fp8", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes", "fa_fwd_varlen", "fa_last_error",
          "fa_quantize_fp8", "fa_status_string", "fa_version"])
 
@@ -135,6 +135,34 @@ def test_bwd_argument_errors(lib, kw, code, text):
     args.update(kw)
     assert binding.fa_bwd_atomic(*args.values()) == code
     assert text in binding.fa_last_error()
+
+
+def bwd_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, batch=1, n_q_heads=2, n_kv_heads=1,
+                seqlen_q=16, seqlen_k=16, head_dim=64, scale=0.125, causal=0, in_dtype=1, o_dtype=1, grad_dtype=1,
+                precision=0, stream=None)
+    args.update(kw)
+    return binding.fa_bwd_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(dq=0), INVALID, "dq is NULL"),
+    (dict(dv=MIS), INVALID, "dv is not 16-byte aligned"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
+    (dict(precision=3), INVALID, "FA_PRECISION"),
+    # more rows than the static scratch holds: rejected before any device call
+    (dict(n_q_heads=2, seqlen_q=(1 << 21) + 1, seqlen_k=16), INVALID, "exceeds its scratch"),
+    (dict(batch=4, n_q_heads=8, n_kv_heads=8, seqlen_q=131073, seqlen_k=131073), INVALID, "exceeds its scratch"),
+])
+def test_bwd_noalloc_argument_errors(lib, kw, code, text):
+    assert bwd_noalloc(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+def test_bwd_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_BWD_NOALLOC_MAX_ROWS 4194304\b", text)
+    assert 4194304 == 1 << 22
 
 
 def test_bwd_atomic_rejects_hilo(lib):
