@@ -291,7 +291,7 @@ int fa_quantize_fp8(const void* x, void* codes, float* block_scales, const signe
   if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
                                                      " unsupported (64 or 128)");
   if ((long long)seqlen * head_dim >= (1LL << 31)) return fail(FA_ERR_INVALID_ARGUMENT, "seqlen * head_dim must be below 2^31");
-  if ((long long)batch * n_heads * ((seqlen + 63) / 64) >= (1LL << 31))
+  if ((long long)batch * n_heads * (((long long)seqlen + 63) / 64) >= (1LL << 31))
     return fail(FA_ERR_INVALID_ARGUMENT, "batch * n_heads * blocks too large");
   hipError_t e = fa::launch_quantize_fp8(x, codes, block_scales, signs, batch * n_heads, seqlen, head_dim,
                                          (hipStream_t)stream);
@@ -334,7 +334,7 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes, 
 
 size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen) {
   if (batch <= 0 || n_heads <= 0 || seqlen <= 0) return 0;
-  return (size_t)batch * (size_t)n_heads * (size_t)((seqlen + 63) / 64);
+  return (size_t)batch * (size_t)n_heads * (((size_t)seqlen + 63) / 64);
 }
 
 size_t fa_bwd_workspace_bytes(int batch, int n_q_heads, int seqlen_q) {

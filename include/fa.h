@@ -39,7 +39,12 @@
  *    products, or carried as bf16 pairs (enum fa_precision, backward); the
  *    scale is applied in fp32 to the fp32 scores, never folded into a rounded
  *    operand. NaN or Inf in an input row propagates to the outputs that
- *    depend on it.
+ *    depend on it; masked scores are replaced, not multiplied, so a NaN key
+ *    row does not reach the causal rows before it. Where a product spans a
+ *    whole tile, a NaN also reaches outputs of the same tile through a zero
+ *    factor: a NaN in query row i sets dK_j to NaN for the keys i < j <=
+ *    32 * floor(i / 32) + 31 as well (the dK/dV pass multiplies aligned
+ *    32-row blocks of Q, and 0 * NaN is NaN).
  */
 #ifndef FA_H_
 #define FA_H_

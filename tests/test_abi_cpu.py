@@ -414,3 +414,29 @@ def test_tile_bookkeeping_matches_brute_force():
     assert n_cls > 500 and n_trip > 500
     for (units, items), pairs in seen.items():
         assert len(pairs) == units * items, "xcd_decode must be a bijection"
+
+
+def test_abi_under_host_sanitizers(tmp_path):
+    """The C ABI (fa_api.cpp with fa_args.h) built by g++ with the address and
+    undefined-behaviour sanitizers, the kernel launchers replaced by stubs
+    (tests/host/launch_stubs.cpp), driven through valid and invalid calls at
+    the edges of the 32-bit sizes (tests/host/abi_driver.cpp): it must run to
+    the end with every expectation met and no sanitizer report."""
+    import shutil
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "abi_driver"
+    csrc = os.path.join(ROOT, "exact_tiled_attention_28_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}", os.path.join(csrc, "fa_api.cpp"),
+           os.path.join(ROOT, "tests", "host", "launch_stubs.cpp"),
+           os.path.join(ROOT, "tests", "host", "abi_driver.cpp"), "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi driver ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
