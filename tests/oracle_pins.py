@@ -133,46 +133,70 @@ def pin_two_block_identity(ora):
         assert np.max(np.abs(Lc - L)) <= 1e-12, "two-block recurrence differs from direct L"
 
 
-def tiled_forward(Q, K, V, s, Br, Bc, causal):
-    """The page-6.2 section 6.1 loop in float64: Q tiles outside, K/V tiles
-    inside up to kv_end = min(N, i + Br) when causal, element mask only on
-    tiles with i < j + Bc - 1, unnormalised accumulator rescaled by
-    exp(m_old - m_new), one division at the end, L = m + log l."""
+def _tile_partial(Qi, Kj, Vj, s, rows, cols, causal):
+    """Softmax statistics of one (Q tile, K/V tile) pair on its own: the
+    tile's row max m, its row sum l = sum exp(S - m) and the unnormalised
+    output O~ = exp(S - m) V_j. Rows that see no key of the tile get m = -inf,
+    l = 0, O~ = 0."""
+    S = s * (Qi @ Kj.T)
+    if causal:
+        S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+    m = S.max(axis=1)
+    base = np.where(np.isfinite(m), m, 0.0)
+    E = np.exp(S - base[:, None])
+    return m, E.sum(axis=1), E @ Vj
+
+
+def _merge(a, b):
+    """Combine the statistics of two disjoint key sets (the rescaling of the
+    CSDN article's two-block derivation, in either order): m = max(m1, m2),
+    l = e^{m1-m} l1 + e^{m2-m} l2, O~ = e^{m1-m} O~1 + e^{m2-m} O~2."""
+    (m1, l1, o1), (m2, l2, o2) = a, b
+    m = np.maximum(m1, m2)
+    base = np.where(np.isfinite(m), m, 0.0)
+    w1, w2 = np.exp(m1 - base), np.exp(m2 - base)
+    return m, w1 * l1 + w2 * l2, w1[:, None] * o1 + w2[:, None] * o2
+
+
+def tiled_forward(Q, K, V, s, Br, Bc, causal, rng=None):
+    """Forward by tiles: for each Q tile of Br rows, the statistics of every
+    K/V tile of Bc keys it must visit, merged in a random order (tree-like,
+    not left to right), then O = O~ / l and L = m + log l. Under the causal
+    mask, K/V tiles whose first key lies after the Q tile's last row are not
+    visited at all (page 6.2, section 5.3: the block-skip rule); tiles that
+    cross the diagonal are masked element by element. Equal to the plain
+    definition for any Br, Bc and merge order, which is what the pin checks."""
+    rng = rng or np.random.default_rng(0)
     N, d = Q.shape
     O = np.zeros((N, d))
     L = np.zeros(N)
     for i in range(0, N, Br):
-        Qi = Q[i:i + Br]
-        n = Qi.shape[0]
-        m = np.full(n, -np.inf)
-        ell = np.zeros(n)
-        Ot = np.zeros((n, d))
-        kv_end = min(N, i + Br) if causal else K.shape[0]
-        for j in range(0, kv_end, Bc):
-            Kj, Vj = K[j:j + Bc], V[j:j + Bc]
-            S = s * (Qi @ Kj.T)
-            if causal and i < j + Bc - 1:
-                rows = i + np.arange(n)[:, None]
-                cols = j + np.arange(Kj.shape[0])[None, :]
-                S = np.where(cols > rows, -np.inf, S)
-            m_new = np.maximum(m, S.max(axis=1))
-            P = np.exp(S - m_new[:, None])
-            ell = np.exp(m - m_new) * ell + P.sum(axis=1)
-            Ot = np.exp(m - m_new)[:, None] * Ot + P @ Vj
-            m = m_new
-        O[i:i + n] = Ot / ell[:, None]
-        L[i:i + n] = m + np.log(ell)
+        rows = np.arange(i, min(N, i + Br))
+        parts = []
+        for j in range(0, K.shape[0], Bc):
+            cols = np.arange(j, min(K.shape[0], j + Bc))
+            if causal and cols[0] > rows[-1]:
+                continue  # the whole tile lies above the diagonal
+            parts.append(_tile_partial(Q[rows], K[cols], V[cols], s, rows, cols, causal))
+        while len(parts) > 1:
+            a, b = sorted(rng.choice(len(parts), size=2, replace=False))
+            merged = _merge(parts[a], parts[b])
+            parts = [p for t, p in enumerate(parts) if t not in (a, b)] + [merged]
+        m, ell, Ot = parts[0]
+        O[rows] = Ot / ell[:, None]
+        L[rows] = m + np.log(ell)
     return O, L
 
 
 def pin_tiled_loop(ora):
     q, k, v, _ = _rng_inputs(6, 1, 1, 1, 37, 37, 5)
     qh, kh, vh = q[0, 0], k[0, 0], v[0, 0]
+    rng = np.random.default_rng(6)
     for causal in (False, True):
         O, L = ora.forward_head(qh, kh, vh, 0.6, causal)
-        for Br, Bc in [(8, 8), (16, 4), (4, 16), (37, 37), (5, 7)]:
-            Ot, Lt = tiled_forward(qh, kh, vh, 0.6, Br, Bc, causal)
-            assert np.max(np.abs(Ot - O)) <= 1e-12, f"tiled loop differs (Br={Br}, Bc={Bc})"
+        for Br, Bc in [(8, 8), (16, 4), (4, 16), (37, 37), (5, 7), (1, 1)]:
+            Ot, Lt = tiled_forward(qh, kh, vh, 0.6, Br, Bc, causal, rng)
+            assert np.max(np.abs(Ot - O)) <= 1e-12, f"tiled forward differs (Br={Br}, Bc={Bc})"
             assert np.max(np.abs(Lt - L)) <= 1e-12
 
 
