@@ -2,21 +2,35 @@
 """Benchmark of the attention hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-fa_fwd (bf16 O, fp32 L) followed by fa_bwd (D preprocess, dK/dV kernel,
-dQ kernel; fp32 dQ, bf16 dK/dV) on the causal bf16 workload B=8, H=16, N=2048, d=128
-(seed 2), inputs resident in HBM. Prints ONE JSON line.
+fa_fwd (bf16 O, fp32 L) followed by fa_bwd (dQ pass forming D, then the dK/dV
+pass; fp32 dQ, bf16 dK/dV, bf16 P and dS) on the causal bf16 backward
+workload B=4, H=16, N=4096, d=128 (seed 5), whose O and L come from that
+forward. Inputs are resident in HBM before the timed region; L2 and MALL are
+not flushed between calls. Prints ONE JSON line.
 
 value = causal-adjusted TFLOPS of the step: forward 4*B*H*N^2*d/2 plus
-backward 2.5x that, divided by the step time. Forward and backward TFLOPS
-and their fractions of the dense bf16 MFMA peak are reported separately.
+backward 2.5x that, divided by the wall-clock time of the timed steps
+(synchronised on both sides). Forward and backward times come from HIP
+events recorded between the calls on the launch stream.
 
-`roofline` covers the call that takes the most time per step, timed with HIP
-events recorded on the stream the library launches on. `cpu_baseline` times
-the fp64 CPU oracle (forward + backward) on a bounded sample of the same
-workload: a few (batch, head) slices.
+Also in the line:
+* `configs`: every named workload (forward configs, the backward config)
+  timed on its own with at least --config-calls calls: median / min / p90,
+  TFLOPS and % of the dense bf16 MFMA peak, both the published one and the
+  one at the shader clock measured while that workload ran;
+* `gpu_clock_mhz`: the shader clock read from `amd-smi metric --clock` by a
+  child process started before the GPU is touched, over a window of
+  back-to-back steps (the timed region itself is too short for the tool's
+  refresh period);
+* `roofline`: the call that takes the most time per step (fa_bwd), timed
+  with HIP events on the stream the library launches on, with the HBM bytes
+  per launch recorded from rocprofv3 counters for the same kernel sources;
+* `cpu_baseline`: the fp64 CPU oracle on a bounded sample of the step's
+  workload (plus a sample of every other workload under `per_config`), with
+  the CPU model and the BLAS library and thread count.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload NAME   (one of the named workloads, extra)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs] [--no-clock]
+       python bench.py --workload NAME | --varlen | --sweep | --persistent | --fp8   (extra measurements)
 """
 
 from __future__ import annotations
@@ -24,55 +38,182 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# Copy-calibrated HBM bytes per launch of the step's calls, written by
-# --summarize-profiles from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "fa_step_b8_h16_n2048_d128_hbm_bytes.json")
+# Per-launch kernel durations and HBM bytes of the step's calls, written by
+# --summarize-profiles from rocprofv3 runs of this benchmark.
+PROFILE_JSON = os.path.join(ROOT, "profiles", "fa_step_b4_h16_n4096_d128_profile.json")
 sys.path.insert(0, ROOT)
 
 from exact_tiled_attention_28_amd import binding  # noqa: E402
 from exact_tiled_attention_28_amd.inputs import make_inputs  # noqa: E402
 from exact_tiled_attention_28_amd.workloads import (  # noqa: E402
-    MI355X_BF16_PEAK_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, bwd_bytes, bwd_flops, fwd_bytes, fwd_flops)
+    MI355X_BF16_PEAK_TFLOPS, WORKLOAD_ORDER, WORKLOADS, bwd_bytes, bwd_flops, fwd_bytes, fwd_flops,
+    workload_bytes, workload_flops)
 
 METRIC = "attention fwd/bwd TFLOPS (causal-adjusted) and % of MI355X bf16 MFMA peak"
-STEP_WORKLOAD = "fwd_bf16_causal_b8_h16_n2048_d128"
+STEP_WORKLOAD = "bwd_bf16_causal_b4_h16_n4096_d128"
+# Dense bf16 MFMA flops per clock of the whole chip: 256 CUs x 4096.
+BF16_FLOPS_PER_CLK = 256 * 4096
+# (batch, head) slices of each workload timed on the CPU oracle: about 20 s
+# of fp64 work in all on 16 host threads.
+CPU_SLICES = {
+    "fwd_f32_b1_h1_n128_d64": 1,
+    "fwd_bf16_causal_b8_h16_n2048_d128": 16,
+    "fwd_bf16_causal_b1_h8_n16384_d128": 2,
+    "fwd_bf16_causal_gqa_b4_hq32_hkv8_n4096_d128_outliers": 4,
+    "bwd_bf16_causal_b4_h16_n4096_d128": 32,
+}
+CACHE_NOTE = ("inputs resident in HBM before timing; L2 and MALL are not flushed between timed calls (the step "
+              "reads 256 MiB of Q, K, V, dO, as large as the 256 MiB MALL before its outputs are counted)")
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--no-others", action="store_true",
-                   help="skip timing the other named workloads after the step (profiled runs of the step use this)")
-    p.add_argument("--cpu-heads", type=int, default=128, help="(batch, head) slices timed on the CPU oracle")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip timing the named workloads one by one after the step (profiled runs use this)")
+    p.add_argument("--no-clock", action="store_true",
+                   help="do not sample the shader clock (profiled runs use this: no child process)")
+    p.add_argument("--config-calls", type=int, default=50, help="timed calls per named workload")
+    p.add_argument("--clock-window", type=float, default=2.0,
+                   help="seconds of back-to-back steps over which the shader clock is read (half of it per "
+                        "named workload)")
     p.add_argument("--workload", default=None, help="time one named workload (fwd or bwd only)")
     p.add_argument("--varlen", action="store_true", help="time fa_fwd_varlen + fa_bwd_varlen on a packed batch")
     p.add_argument("--sweep", action="store_true",
                    help="fa_fwd / fa_bwd throughput over head dim 64/128, N 1K-32K, causal and not, MHA and GQA")
     p.add_argument("--persistent", action="store_true",
-                   help="time fa_fwd_persistent beside fa_fwd (default forward workload, or --workload)")
+                   help="time fa_fwd_persistent beside fa_fwd (forward workload B8 H16 N2048, or --workload)")
     p.add_argument("--fp8", action="store_true",
-                   help="time fa_quantize_fp8 (Q and K) + fa_fwd_fp8 beside fa_fwd (default workload, or --workload)")
+                   help="time fa_quantize_fp8 (Q and K) + fa_fwd_fp8 beside fa_fwd (B8 H16 N2048, or --workload)")
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
-                   help="summarise rocprofv3 output under DIR/{trace,fetch,write} (no GPU needed) and record "
-                        "the HBM bytes per launch for the current kernel sources")
+                   help="summarise rocprofv3 output under DIR/{trace,fetch,write,rdreq,tcc} (no GPU needed) and "
+                        "record per-launch durations and HBM bytes for the current kernel sources")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR",
-                   help="summarise a rocprofv3 --pmc run of SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
-                        "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE under DIR (no GPU needed)")
+                   help="summarise a rocprofv3 --pmc run of the SQ counters under DIR (no GPU needed)")
     p.add_argument("--calibration-mib", type=int, default=256, help="copy size used by the counter runs")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, copy a MIB-MiB buffer 3 times (a plain copy kernel of known size, to "
                         "scale the HBM byte counters of a profiler run)")
-    return p.parse_args()
+    p.add_argument("--poll-clock", type=float, default=None, metavar="SECONDS", help=argparse.SUPPRESS)
+    return p.parse_args(argv)
 
+
+# ---------------------------------------------------------------- shader clock
+
+def read_amd_smi_clock(text):
+    """Per-XCD shader clocks (MHz) from `amd-smi metric -g 0 --clock --json`
+    output, or None when the text holds none."""
+    starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
+    if not starts:
+        return None
+    try:
+        d = json.loads(text[min(starts):])
+    except json.JSONDecodeError:
+        return None
+    gpus = d.get("gpu_data", []) if isinstance(d, dict) else d
+    if not gpus or not isinstance(gpus[0], dict):
+        return None
+    clk = gpus[0].get("clock", {})
+    mhz = []
+    for key in sorted(k for k in clk if k.startswith("gfx_")):
+        v = clk[key].get("clk", {}) if isinstance(clk[key], dict) else {}
+        v = v.get("value") if isinstance(v, dict) else None
+        if isinstance(v, (int, float)):
+            mhz.append(float(v))
+    return mhz or None
+
+
+def poll_clock_main(period):
+    """Child-process loop: print `time mean min max` (MHz over the XCDs) about
+    every `period` seconds until the parent goes away. Touches no HIP API."""
+    parent = os.getppid()
+    t_stop = time.time() + 1800
+    while time.time() < t_stop and os.getppid() == parent:
+        t0 = time.time()
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                               text=True, timeout=10)
+        except (OSError, subprocess.SubprocessError):
+            return
+        mhz = read_amd_smi_clock(r.stdout)
+        if mhz:
+            t = (t0 + time.time()) / 2
+            print(f"{t:.3f} {np.mean(mhz):.1f} {min(mhz):.1f} {max(mhz):.1f}", flush=True)
+        time.sleep(max(0.0, period - (time.time() - t0)))
+
+
+class ClockPoller:
+    """Shader-clock samples from a child process running amd-smi. Started
+    before this process touches the GPU, so no process that holds a GPU
+    context ever forks or execs."""
+
+    def __init__(self, period=0.1):
+        self.samples = []  # (time, mean MHz, min MHz, max MHz)
+        self.proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--poll-clock", str(period)],
+                                     stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        self.reader = threading.Thread(target=self._read, daemon=True)
+        self.reader.start()
+
+    def _read(self):
+        for line in self.proc.stdout:
+            f = line.split()
+            if len(f) == 4:
+                self.samples.append(tuple(float(x) for x in f))
+
+    def window(self, t0, t1):
+        """Clock statistics over the samples taken between t0 and t1."""
+        return clock_window(self.samples, t0, t1)
+
+    def stop(self):
+        if self.proc.poll() is None:
+            self.proc.terminate()
+            try:
+                self.proc.wait(timeout=5)
+            except subprocess.TimeoutExpired:
+                self.proc.kill()
+
+
+def clock_window(samples, t0, t1):
+    """Median of the per-sample XCD-mean clocks taken between t0 and t1, the
+    lowest and highest single-XCD reading, and the sample count; None when
+    no sample falls in the window."""
+    s = [x for x in samples if t0 <= x[0] <= t1]
+    if not s:
+        return None
+    return {"median": round(float(np.median([x[1] for x in s])), 1), "min_xcd": round(min(x[2] for x in s), 1),
+            "max_xcd": round(max(x[3] for x in s), 1), "samples": len(s)}
+
+
+def peak_at_clock(mhz):
+    """Dense bf16 MFMA peak (TFLOP/s) at a shader clock of `mhz`."""
+    return BF16_FLOPS_PER_CLK * mhz * 1e6 / 1e12
+
+
+def run_for(calls, seconds):
+    """Issue `calls` back to back for about `seconds` (untimed load under
+    which the clock is read); returns (start, end) wall times."""
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+    return t0, time.time()
+
+
+# ---------------------------------------------------------------- device state
 
 def device_inputs(w, with_do):
     import torch
@@ -126,17 +267,18 @@ class Step:
         w = self.w
         fn = fn or binding.fa_bwd
         rc = fn(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
-                            self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
-                            self.dv.data_ptr(), self.ws.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen,
-                            w.seqlen, w.head_dim, w.scale, int(w.causal), self.code, self.code, self.code,
-                            self.precision, self.sh)
+                self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
+                self.dv.data_ptr(), self.ws.data_ptr(), w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen,
+                w.seqlen, w.head_dim, w.scale, int(w.causal), self.code, self.code, self.code,
+                self.precision, self.sh)
         if rc:
             raise binding.FAError(rc, fn.__name__, binding.fa_last_error())
 
 
 def time_calls(step, calls, steps, warmup):
     """Run `calls` (a list of callables) per step; return the step times and
-    per-call times (ms) from HIP events recorded on the launch stream."""
+    per-call times (ms) from HIP events recorded on the launch stream, and
+    the wall-clock ms per step over the synchronised timed region."""
     import torch
     stream = step.stream if step is not None else torch.cuda.current_stream()
     for _ in range(warmup):
@@ -158,11 +300,97 @@ def time_calls(step, calls, steps, warmup):
     return per_step, per_call, wall
 
 
+def time_stats(ms, flops, nbytes, clock):
+    """Summary of one call's timed durations (ms): median, min, p90, mean,
+    throughput at the median, and % of peak (published, and at `clock`)."""
+    ms = np.asarray(ms, dtype=np.float64)
+    med = float(np.median(ms))
+    tf = flops / (med * 1e-3) / 1e12
+    out = {"calls": int(len(ms)), "ms_median": round(med, 4), "ms_min": round(float(ms.min()), 4),
+           "ms_p90": round(float(np.percentile(ms, 90)), 4), "ms_mean": round(float(ms.mean()), 4),
+           "tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / MI355X_BF16_PEAK_TFLOPS, 2),
+           "gbps_algorithmic": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    if clock:
+        out["clock_mhz"] = clock["median"]
+        out["pct_of_bf16_peak_at_clock"] = round(100 * tf / peak_at_clock(clock["median"]), 2)
+    return out
+
+
+def time_config(w, calls_n, warmup, poller, window_s):
+    """Time one named workload's pass (`calls_n` calls after `warmup`), then
+    read the clock under `window_s` seconds of the same calls."""
+    inp, q, k, v, do = device_inputs(w, with_do=w.passes == "bwd")
+    step = Step(w, q, k, v, do if do is not None else q)
+    if w.passes == "bwd":
+        step.fwd()
+        calls = [step.bwd]
+    else:
+        calls = [step.fwd]
+    per_step, _, _ = time_calls(step, calls, calls_n, warmup)
+    clock = None
+    if poller is not None:
+        t0, t1 = run_for(calls, window_s)
+        clock = poller.window(t0 + 0.25 * window_s, t1)
+    res = time_stats(per_step, workload_flops(w), workload_bytes(w), clock)
+    res["pass"] = "fa_bwd" if w.passes == "bwd" else "fa_fwd"
+    return inp, res
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def host_description():
+    """CPU model, logical CPUs this process may use, and the BLAS numpy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            threads = int(i.get("num_threads", threads))
+            blas = (f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')} kernels, "
+                    f"{i.get('threading_layer')} threads)")
+    except Exception:
+        pass
+    return {"cpu_model": model, "logical_cpus": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": threads}
+
+
+def cpu_oracle_sample(w, inp, slices, with_bwd):
+    """Time the fp64 oracle, untuned, on the first `slices` (batch, head)
+    slices of workload `w`: forward, plus backward when `with_bwd`.
+    Returns (TFLOPS on the causal-adjusted count, seconds, slices)."""
+    import oracle
+    sel = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)][:slices]
+    t0 = time.perf_counter()
+    for b, h in sel:
+        g = h // w.group
+        oracle.forward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], w.scale, w.causal)
+        if with_bwd:
+            oracle.backward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], inp.do[b, h], w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    fl = fwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    if with_bwd:
+        fl += bwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal)
+    return len(sel) * fl / dt / 1e12, dt, len(sel)
+
+
+# ---------------------------------------------------------------- extra modes
+
 # Packed variable-length batch timed by --varlen: 16 causal sequences whose
 # lengths are drawn uniformly from [256, 4096] (seed 11), Hq = Hkv = 16,
 # d = 128, bf16 (a mix like the unequal-length batches the FlashAttention-3
 # news page names; no dataset is involved).
 VARLEN_SEED, VARLEN_SEQS, VARLEN_MIN, VARLEN_MAX, VARLEN_H, VARLEN_D = 11, 16, 256, 4096, 16, 128
+DEFAULT_FWD = "fwd_bf16_causal_b8_h16_n2048_d128"
 
 
 def bench_varlen(args):
@@ -281,7 +509,7 @@ def bench_persistent(args):
     """Time fa_fwd_persistent (work-queue grid) and fa_fwd (one workgroup per
     item) on the same forward workload; prints one JSON line."""
     import torch
-    w = WORKLOADS[args.workload or STEP_WORKLOAD]
+    w = WORKLOADS[args.workload or DEFAULT_FWD]
     if w.passes != "fwd" or w.dtype != "bf16":
         raise SystemExit(f"--persistent needs a bf16 forward workload, not {w.name}")
     _, q, k, v, _ = device_inputs(w, with_do=False)
@@ -315,7 +543,7 @@ def bench_fp8(args):
     and O = P V at the bf16 peak: half of the flops each."""
     import torch
     from exact_tiled_attention_28_amd.inputs import make_signs
-    w = WORKLOADS[args.workload or STEP_WORKLOAD]
+    w = WORKLOADS[args.workload or DEFAULT_FWD]
     if w.passes != "fwd" or w.head_dim != 128 or w.dtype != "bf16":
         raise SystemExit(f"--fp8 needs a bf16 forward workload with head_dim 128, not {w.name}")
     _, q, k, v, _ = device_inputs(w, with_do=False)
@@ -359,6 +587,15 @@ def bench_fp8(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_one(args):
+    """Time one named workload's pass (fwd or bwd); prints one JSON line."""
+    _, res = time_config(WORKLOADS[args.workload], args.steps, args.warmup, None, 0)
+    res["workload"] = args.workload
+    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------- profiles
+
 def csrc_sha256():
     """sha256 over the kernel sources (file names and contents, sorted)."""
     import hashlib
@@ -392,7 +629,7 @@ def _template_args(kernel):
 
 # Position of the VARLEN / PERSIST template argument of each kernel template
 # (fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>,
-# bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN>, bwd_dq_kernel<D, CAUSAL, VARLEN, NW>).
+# bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN, HILO>, bwd_dq_kernel<D, CAUSAL, VARLEN, NW, HILO>).
 _VARLEN_ARG = {
     "void fa::fwd_kernel<": 5,
     "void fa::bwd_dkdv_kernel<": 3,
@@ -418,27 +655,46 @@ def _call_of(kernel):
     return None
 
 
-def summarize_profiles(prof_dir, calib_mib, out_path=None):
-    """Turn the rocprofv3 output of one kernel-trace run (prof_dir/trace) and
-    two counter runs (prof_dir/fetch: FETCH_SIZE, prof_dir/write: WRITE_SIZE,
-    each with --copy-calibration calib_mib) into markdown tables, and record
-    the copy-calibrated HBM bytes per launch of fa_fwd / fa_bwd for the
-    current kernel sources in TRAFFIC_JSON."""
+def _csv_rows(prof_dir, sub, suffix):
     import csv
     import glob
+    files = glob.glob(os.path.join(prof_dir, sub, "*" + suffix))
+    if not files:
+        return None
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
 
-    def rows(sub, suffix):
-        files = glob.glob(os.path.join(prof_dir, sub, "*" + suffix))
-        if not files:
-            raise SystemExit(f"no *{suffix} under {os.path.join(prof_dir, sub)}")
-        with open(files[0]) as fh:
-            return list(csv.DictReader(fh))
 
-    stats = rows("trace", "kernel_stats.csv")
+def _counter_means(rows, names):
+    """Mean over dispatches of each counter in `names`, per kernel name."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] not in names:
+            continue
+        k = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})
+        k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {kern: {c: sum(v.values()) / len(v) for c, v in per.items()} for kern, per in acc.items()}
+
+
+RDREQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+TCC_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_sum")
+
+
+def summarize_profiles(prof_dir, calib_mib, out_path=None):
+    """Turn the rocprofv3 output of one kernel-trace run (prof_dir/trace) and
+    the counter runs (prof_dir/fetch: FETCH_SIZE, prof_dir/write: WRITE_SIZE,
+    prof_dir/rdreq: RDREQ_COUNTERS, prof_dir/tcc: TCC_COUNTERS; each with
+    --copy-calibration calib_mib) into markdown tables on stdout, and record
+    per-launch kernel durations and HBM bytes of each entry point for the
+    current kernel sources in PROFILE_JSON (or out_path). Counter runs that
+    are absent are skipped."""
+    stats = _csv_rows(prof_dir, "trace", "kernel_stats.csv")
+    if stats is None:
+        raise SystemExit(f"no *kernel_stats.csv under {os.path.join(prof_dir, 'trace')}")
     total = sum(float(r["TotalDurationNs"]) for r in stats)
     print("| kernel | entry point | calls | average µs | min µs | max µs | share |")
     print("|---|---|---|---|---|---|---|")
-    per_call_us = {}
+    per_call = {}
     for r in stats:
         name = r["Name"]
         call = _call_of(name)
@@ -446,69 +702,124 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
         print(f"| `{name}` | {call or '-'} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
               f"{float(r['MaxNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
         if call:
-            per_call_us[call] = per_call_us.get(call, 0.0) + avg
-    print()
-    for call, us in sorted(per_call_us.items()):
-        print(f"- `{call}`: sum of its kernels' average durations {us:.1f} µs")
-    print()
-
-    if not os.path.isdir(os.path.join(prof_dir, "fetch")):
-        return  # a kernel-trace-only run
-    counters = {}
-    for sub, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
-        acc = {}
-        for r in rows(sub, "counter_collection.csv"):
-            if r["Counter_Name"] != cname:
-                continue
-            k = acc.setdefault(r["Kernel_Name"], {})
-            k[r["Dispatch_Id"]] = k.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-        counters[cname] = {name: sum(v.values()) / len(v) for name, v in acc.items()}
-    calib_kib = calib_mib * 1024
-    scale = {}
-    for cname, per in counters.items():
-        copies = [v for name, v in per.items() if "copyBuffer" in name]
-        if not copies:
-            raise SystemExit(f"{cname}: no copy kernel in the counter run (run it with --copy-calibration)")
-        scale[cname] = calib_kib / (sum(copies) / len(copies))
-    print(f"Calibration: a copy of {calib_mib} MiB reads {calib_kib / scale['FETCH_SIZE']:.0f} KiB of FETCH_SIZE "
-          f"(scale x{scale['FETCH_SIZE']:.4f}) and {calib_kib / scale['WRITE_SIZE']:.0f} KiB of WRITE_SIZE "
-          f"(scale x{scale['WRITE_SIZE']:.4f}).")
-    print()
-    print("| kernel | entry point | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) |")
-    print("|---|---|---|---|---|")
-    per_call = {}
-    names = sorted(set(counters["FETCH_SIZE"]) | set(counters["WRITE_SIZE"]))
-    for name in names:
-        call = _call_of(name)
-        if call is None:
-            continue
-        f = counters["FETCH_SIZE"].get(name, 0.0)
-        wr = counters["WRITE_SIZE"].get(name, 0.0)
-        fb, wb = f * 1024 * scale["FETCH_SIZE"], wr * 1024 * scale["WRITE_SIZE"]
-        print(f"| `{name}` | {call} | {f:.0f} | {wr:.0f} | {(fb + wb) / 1e6:.0f} |")
-        c = per_call.setdefault(call, {"fetch_bytes": 0, "write_bytes": 0})
-        c["fetch_bytes"] += int(round(fb))
-        c["write_bytes"] += int(round(wb))
+            c = per_call.setdefault(call, {"kernel_avg_us": 0.0})
+            c["kernel_avg_us"] = round(c["kernel_avg_us"] + avg, 2)
     print()
     for call, c in sorted(per_call.items()):
-        print(f"- `{call}`: {(c['fetch_bytes'] + c['write_bytes']) / 1e6:.0f} MB per launch")
-    rec = {"note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per dispatch), "
-                   "scaled by the same counters on a copy of known size",
-           "kernel_sources_sha256": csrc_sha256(), "workload": "fwd_bf16_causal_b8_h16_n2048_d128",
-           "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4)}
-    rec.update({k: v for k, v in per_call.items() if k in ("fa_fwd", "fa_bwd")})
-    out_path = out_path or TRAFFIC_JSON
+        print(f"- `{call}`: sum of its kernels' average durations {c['kernel_avg_us']:.1f} µs")
+    print()
+    rec = {"note": "per launch of each entry point: the sum of its kernels' average durations (rocprofv3 "
+                   "--kernel-trace --stats); HBM bytes from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per "
+                   "dispatch) scaled by the same counters on a copy of known size; read bytes counted from "
+                   "TCC_EA0_RDREQ by request size; L2 hits and misses",
+           "kernel_sources_sha256": csrc_sha256(), "workload": STEP_WORKLOAD}
+
+    calib_kib = calib_mib * 1024
+
+    def copy_scale(per, cname):
+        copies = [v[cname] for name, v in per.items() if "copyBuffer" in name and cname in v]
+        if not copies:
+            raise SystemExit(f"{cname}: no copy kernel in the counter run (run it with --copy-calibration)")
+        return calib_kib / (sum(copies) / len(copies))
+
+    fetch_scaled = {}  # kernel name -> copy-calibrated FETCH_SIZE bytes per dispatch
+    fetch = _csv_rows(prof_dir, "fetch", "counter_collection.csv")
+    write = _csv_rows(prof_dir, "write", "counter_collection.csv")
+    if fetch is not None and write is not None:
+        fmeans = _counter_means(fetch, {"FETCH_SIZE"})
+        wmeans = _counter_means(write, {"WRITE_SIZE"})
+        sf, sw = copy_scale(fmeans, "FETCH_SIZE"), copy_scale(wmeans, "WRITE_SIZE")
+        print(f"Calibration: a copy of {calib_mib} MiB reads {calib_kib / sf:.0f} KiB of FETCH_SIZE "
+              f"(scale x{sf:.4f}) and {calib_kib / sw:.0f} KiB of WRITE_SIZE (scale x{sw:.4f}).")
+        print()
+        print("| kernel | entry point | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB (scaled) |")
+        print("|---|---|---|---|---|")
+        for name in sorted(set(fmeans) | set(wmeans)):
+            call = _call_of(name)
+            if call is None:
+                continue
+            f = fmeans.get(name, {}).get("FETCH_SIZE", 0.0)
+            wr = wmeans.get(name, {}).get("WRITE_SIZE", 0.0)
+            fb, wb = f * 1024 * sf, wr * 1024 * sw
+            fetch_scaled[name] = fb
+            print(f"| `{name}` | {call} | {f:.0f} | {wr:.0f} | {(fb + wb) / 1e6:.0f} |")
+            c = per_call.setdefault(call, {})
+            c["fetch_bytes"] = c.get("fetch_bytes", 0) + int(round(fb))
+            c["write_bytes"] = c.get("write_bytes", 0) + int(round(wb))
+        print()
+        rec["fetch_scale"], rec["write_scale"] = round(sf, 4), round(sw, 4)
+
+    rdreq = _csv_rows(prof_dir, "rdreq", "counter_collection.csv")
+    if rdreq is not None:
+        means = _counter_means(rdreq, set(RDREQ_COUNTERS))
+        print("Read bytes counted from the requests the L2 sends to the fabric, by size "
+              "(32 x n32 + 64 x n64 + 128 x n128; 'unsized' = requests minus the three sized counts):")
+        print()
+        print("| kernel | entry point | requests | 32 B | 64 B | 128 B | unsized | read MB | "
+              "FETCH_SIZE-scaled MB |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for name, m in sorted(means.items()):
+            call = _call_of(name) or ("copy" if "copyBuffer" in name else None)
+            if call is None:
+                continue
+            n, n32, n64, n128 = (m.get(s, 0.0) for s in RDREQ_COUNTERS)
+            rb = 32 * n32 + 64 * n64 + 128 * n128
+            fs = fetch_scaled.get(name)
+            print(f"| `{name}` | {call} | {n:.0f} | {n32:.0f} | {n64:.0f} | {n128:.0f} | "
+                  f"{n - n32 - n64 - n128:.0f} | {rb / 1e6:.0f} | {'-' if fs is None else f'{fs / 1e6:.0f}'} |")
+            if call != "copy":
+                c = per_call.setdefault(call, {})
+                c["read_bytes_by_request_size"] = c.get("read_bytes_by_request_size", 0) + int(round(rb))
+        print()
+
+    tcc = _csv_rows(prof_dir, "tcc", "counter_collection.csv")
+    if tcc is not None:
+        means = _counter_means(tcc, set(TCC_COUNTERS))
+        print("L2 (TCC) hits and misses, and read requests sent towards DRAM (the memory-side MALL sits "
+              "behind this point, so a DRAM request may still be served by the MALL):")
+        print()
+        print("| kernel | entry point | L2 hits | L2 misses | L2 hit rate | DRAM read requests |")
+        print("|---|---|---|---|---|---|")
+        for name, m in sorted(means.items()):
+            call = _call_of(name) or ("copy" if "copyBuffer" in name else None)
+            if call is None:
+                continue
+            hit, miss, dram = (m.get(s, 0.0) for s in TCC_COUNTERS)
+            rate = hit / (hit + miss) if hit + miss else float("nan")
+            print(f"| `{name}` | {call} | {hit:.0f} | {miss:.0f} | {100 * rate:.1f}% | {dram:.0f} |")
+            if call != "copy":
+                c = per_call.setdefault(call, {})
+                c["l2_hits"] = c.get("l2_hits", 0) + int(round(hit))
+                c["l2_misses"] = c.get("l2_misses", 0) + int(round(miss))
+                c["dram_read_requests"] = c.get("dram_read_requests", 0) + int(round(dram))
+        print()
+
+    for call, c in sorted(per_call.items()):
+        if "fetch_bytes" in c:
+            print(f"- `{call}`: {(c['fetch_bytes'] + c['write_bytes']) / 1e6:.0f} MB of HBM traffic per launch "
+                  f"(copy-calibrated FETCH_SIZE + WRITE_SIZE)")
+    rec.update(per_call)
+    out_path = out_path or PROFILE_JSON
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(f"\nkernel sources sha256 {rec['kernel_sources_sha256']}")
 
 
-def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024):
-    """Per-kernel averages of one rocprofv3 --pmc run: clock (GRBM_GUI_ACTIVE,
-    summed over the n_xcd XCD instances, over the dispatch's duration), MFMA
-    utilisation (SQ_VALU_MFMA_BUSY_CYCLES over n_simd SIMDs x the kernel's
-    cycles, the rocprofv3 MfmaUtil expression), instructions per wavefront,
-    and LDS bank-conflict cycles."""
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_VALU_MFMA_COEXEC_CYCLES",
+               "SQ_ACTIVE_INST_VALU")
+
+
+def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024, n_cu=256):
+    """Per-kernel averages of one rocprofv3 --pmc run of SQ_COUNTERS: clock
+    (GRBM_GUI_ACTIVE, summed over the n_xcd XCD instances, over the
+    dispatch's duration), MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over n_simd
+    SIMDs x the kernel's cycles, rocprofv3's MfmaUtil expression), VALU busy
+    (rocprofv3's VALUBusy expression: SQ_ACTIVE_INST_VALU / n_cu / cycles),
+    co-execution (SQ_VALU_MFMA_COEXEC_CYCLES, cycles in which a SIMD issued a
+    VALU instruction while its MFMA unit was busy, as a share of the MFMA
+    busy cycles), instructions per wavefront and LDS bank-conflict cycles.
+    Counters absent from the run read as zero."""
     import collections
     import csv
     import glob
@@ -522,65 +833,61 @@ def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024):
             d = disp[r["Kernel_Name"]][r["Dispatch_Id"]]
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-    print("| kernel | entry point | dispatches | µs | clock GHz | MFMA busy % | VALU instr / wave | "
-          "MFMA instr / wave | VALU / MFMA | LDS instr / wave | LDS bank-conflict cycles |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| kernel | entry point | dispatches | µs | clock GHz | MFMA busy % | VALU busy % | co-exec % of MFMA "
+          "busy | VALU instr / wave | MFMA instr / wave | VALU / MFMA | LDS instr / wave | LDS bank-conflict "
+          "cycles |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for name, ds in disp.items():
         call = _call_of(name)
         if call is None:
             continue
         n = len(ds)
-        avg = {k: sum(d.get(k, 0.0) for d in ds.values()) / n
-               for k in ("_ns", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_VALU",
-                         "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")}
+        avg = {k: sum(d.get(k, 0.0) for d in ds.values()) / n for k in ("_ns",) + SQ_COUNTERS}
         cyc = avg["GRBM_GUI_ACTIVE"] / n_xcd
         waves = max(avg["SQ_WAVES"], 1.0)
         mfma_busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * n_simd) if cyc else 0.0
+        valu_busy = 100.0 * avg["SQ_ACTIVE_INST_VALU"] / n_cu / cyc if cyc else 0.0
+        coexec = (100.0 * avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+                  if avg["SQ_VALU_MFMA_BUSY_CYCLES"] else float("nan"))
         v_per_m = avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"] if avg["SQ_INSTS_MFMA"] else float("nan")
         print(f"| `{name}` | {call} | {n} | {avg['_ns'] / 1e3:.1f} | {cyc / avg['_ns']:.2f} | {mfma_busy:.1f} | "
-              f"{avg['SQ_INSTS_VALU'] / waves:.0f} | {avg['SQ_INSTS_MFMA'] / waves:.0f} | {v_per_m:.2f} | "
-              f"{avg['SQ_INSTS_LDS'] / waves:.0f} | {avg['SQ_LDS_BANK_CONFLICT']:.0f} |")
+              f"{valu_busy:.1f} | {coexec:.1f} | {avg['SQ_INSTS_VALU'] / waves:.0f} | "
+              f"{avg['SQ_INSTS_MFMA'] / waves:.0f} | {v_per_m:.2f} | {avg['SQ_INSTS_LDS'] / waves:.0f} | "
+              f"{avg['SQ_LDS_BANK_CONFLICT']:.0f} |")
 
 
-def measured_traffic(call):
-    """HBM bytes per launch of `call` ("fa_fwd" / "fa_bwd") recorded from
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel sources
-    have changed since they were taken."""
-    rec_path = TRAFFIC_JSON
-    if not os.path.exists(rec_path):
+def profile_record(call, path=None):
+    """The recorded profile of entry point `call` (kernel durations and HBM
+    bytes per launch), or None when the kernel sources have changed since
+    the profile was taken."""
+    path = path or PROFILE_JSON
+    if not os.path.exists(path):
         return None
-    with open(rec_path) as fh:
+    with open(path) as fh:
         rec = json.load(fh)
     if rec.get("kernel_sources_sha256") != csrc_sha256() or call not in rec:
         return None
-    return rec[call]["fetch_bytes"] + rec[call]["write_bytes"]
+    return rec[call]
 
 
-def cpu_baseline(w, inp, heads):
-    """The fp64 oracle, untuned, on `heads` (batch, head) slices of the
-    workload: forward + backward. Returns the JSON object."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    sel = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)][:heads]
-    t0 = time.perf_counter()
-    for b, h in sel:
-        g = h // w.group
-        oracle.forward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], w.scale, w.causal)
-        oracle.backward_head(inp.q[b, h], inp.k[b, g], inp.v[b, g], inp.do[b, h], w.scale, w.causal)
-    dt = time.perf_counter() - t0
-    flops = heads * (fwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal)
-                     + bwd_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal))
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle forward+backward of {heads} of {w.batch * w.n_q_heads} (batch, head) slices "
-                      f"(N={w.seqlen}, d={w.head_dim}, causal), {dt:.1f} s wall, same causal-adjusted flop count"}
+def copy_calibration(mib):
+    """dst.copy_(src) of `mib` MiB, three times: reads and writes exactly that
+    many bytes per launch."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": mib << 20}), flush=True)
 
+
+# ---------------------------------------------------------------- main
 
 def main():
     args = parse()
+    if args.poll_clock is not None:
+        return poll_clock_main(args.poll_clock)
     if args.summarize_profiles:
         return summarize_profiles(args.summarize_profiles, args.calibration_mib)
     if args.summarize_pmc:
@@ -589,6 +896,18 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the attention path runs on one GPU)", file=sys.stderr)
         sys.exit(2)
+    extra = args.fp8 or args.persistent or args.sweep or args.workload or args.varlen
+    # The clock poller is a child process, started before this process
+    # touches the GPU.
+    poller = None if (args.no_clock or extra) else ClockPoller()
+    try:
+        run(args, poller)
+    finally:
+        if poller is not None:
+            poller.stop()
+
+
+def run(args, poller):
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -607,29 +926,40 @@ def main():
         return bench_varlen(args)
 
     w = WORKLOADS[STEP_WORKLOAD]
+    B, H, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.head_dim
     inp, q, k, v, do = device_inputs(w, with_do=True)
-    if do is None:
-        raise RuntimeError("dO missing")
     step = Step(w, q, k, v, do)
     per_step, per_call, wall = time_calls(step, [step.fwd, step.bwd], args.steps, args.warmup)
-    _, per_call_atomic, _ = time_calls(step, [step.bwd_atomic], args.steps, args.warmup)
-    ms_bwd_atomic = float(np.median(per_call_atomic[:, 0]))
-    ms_step = float(np.median(per_step))
-    ms_fwd = float(np.median(per_call[:, 0]))
-    ms_bwd = float(np.median(per_call[:, 1]))
-    ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
-    bf = bwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
-    tflops = (ff + bf) / (ms_step * 1e-3) / 1e12
-    fwd_tf = ff / (ms_fwd * 1e-3) / 1e12
-    bwd_tf = bf / (ms_bwd * 1e-3) / 1e12
-    avg_fwd = float(np.mean(per_call[:, 0]))
-    avg_bwd = float(np.mean(per_call[:, 1]))
+    clock = None
+    if poller is not None:
+        t0, t1 = run_for([step.fwd, step.bwd], args.clock_window)
+        clock = poller.window(t0 + 0.25 * args.clock_window, t1)
+    ff = fwd_flops(B, H, N, N, d, w.causal)
+    bf = bwd_flops(B, H, N, N, d, w.causal)
+    tflops = (ff + bf) / (wall * 1e-3) / 1e12
+
+    # Roofline of the call that takes the most time per step.
+    avg_fwd, avg_bwd = float(np.mean(per_call[:, 0])), float(np.mean(per_call[:, 1]))
     if avg_bwd >= avg_fwd:
-        dom = {"kernel": "fa_bwd (bwd_dq_kernel with D + bwd_dkdv_kernel, one call)", "flops": bf,
-               "ms": avg_bwd, "traffic": measured_traffic("fa_bwd")}
+        dom = {"call": "fa_bwd", "kernel": "fa_bwd (bwd_dq_kernel forming D and dQ, then bwd_dkdv_kernel)",
+               "flops": bf, "ms": avg_bwd, "bytes": bwd_bytes(B, H, Hkv, N, N, d)}
     else:
-        dom = {"kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd, "traffic": measured_traffic("fa_fwd")}
+        dom = {"call": "fa_fwd", "kernel": "fa_fwd (fwd_kernel)", "flops": ff, "ms": avg_fwd,
+               "bytes": fwd_bytes(B, H, Hkv, N, N, d)}
+    prof = profile_record(dom["call"])
+    traffic = prof["fetch_bytes"] + prof["write_bytes"] if prof and "fetch_bytes" in prof else None
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    roofline = {"kernel": dom["kernel"], "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes": dom["bytes"], "algorithmic_flops": dom["flops"],
+                "avg_launch_ms": round(dom["ms"], 4),
+                "profiled_avg_launch_ms": round(prof["kernel_avg_us"] / 1e3, 4) if prof else None}
+    if clock:
+        roofline["peak_at_clock"] = round(peak_at_clock(clock["median"]), 1)
+        roofline["frac_at_clock"] = round(achieved / roofline["peak_at_clock"], 4)
+
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -637,83 +967,75 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "fa_fwd + fa_bwd, bf16, causal, B=8 Hq=Hkv=16 N=2048 d=128 (seed 2)",
-                   "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-                   "seqlen": w.seqlen, "head_dim": w.head_dim, "causal": w.causal, "parallelism": "single GPU"},
+        "config": {"workload": "backward config B4 H16 N4096 d128 causal bf16 (seed 5): fa_fwd producing O and L, "
+                               "then fa_bwd",
+                   "batch": B, "n_q_heads": H, "n_kv_heads": Hkv, "seqlen": N, "head_dim": d,
+                   "causal": w.causal, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * tflops / MI355X_BF16_PEAK_TFLOPS, 2),
-        "fwd": {"ms": round(ms_fwd, 4), "tflops": round(fwd_tf, 2),
-                "pct_of_bf16_peak": round(100 * fwd_tf / MI355X_BF16_PEAK_TFLOPS, 2),
-                "gbps_algorithmic": round(fwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
-                                                    w.head_dim) / (ms_fwd * 1e-3) / 1e9, 1)},
-        "bwd": {"ms": round(ms_bwd, 4), "tflops": round(bwd_tf, 2),
-                "pct_of_bf16_peak": round(100 * bwd_tf / MI355X_BF16_PEAK_TFLOPS, 2),
-                "gbps_algorithmic": round(bwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen,
-                                                    w.head_dim) / (ms_bwd * 1e-3) / 1e9, 1)},
-        "bwd_atomic_dq": {"ms": round(ms_bwd_atomic, 4),
-                          "tflops": round(bf / (ms_bwd_atomic * 1e-3) / 1e12, 2),
-                          "note": "fa_bwd_atomic: single pass, dQ by fp32 atomics (not in the timed step)"},
-        "wall_ms_per_step": round(wall, 4),
-        "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": dom["traffic"],
-                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-                     "avg_launch_ms": round(dom["ms"], 4)},
+        "ms_per_step_events_median": round(float(np.median(per_step)), 4),
+        "gpu_clock_mhz": clock,
+        "gpu_clock_source": "amd-smi metric -g 0 --clock (mean of the 8 XCD shader clocks), sampled every 0.1 s "
+                            f"over {args.clock_window:.1f} s of back-to-back steps after the timed region, the "
+                            "first quarter dropped",
+        "fwd": time_stats(per_call[:, 0], ff, fwd_bytes(B, H, Hkv, N, N, d), clock),
+        "bwd": time_stats(per_call[:, 1], bf, bwd_bytes(B, H, Hkv, N, N, d), clock),
+        "caches": CACHE_NOTE,
+        "roofline": roofline,
     }
-    # The other named workloads, each pass timed on its own after the step
-    # (context for the same run; not part of value).
-    if not args.no_others:
-        out["other_workloads"] = {name: {k2: v2 for k2, v2 in time_workload(WORKLOADS[name], 10, 3).items()
-                                         if k2 != "workload"}
-                                  for name in WORKLOADS if name != STEP_WORKLOAD}
+    if clock:
+        out["pct_of_bf16_peak_at_clock"] = round(100 * tflops / peak_at_clock(clock["median"]), 2)
+    del step, q, k, v, do
+    torch.cuda.empty_cache()
+
+    cpu = {}
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+        tf, dt, n = cpu_oracle_sample(w, inp, CPU_SLICES[STEP_WORKLOAD], with_bwd=True)
+        cpu[STEP_WORKLOAD] = {"value": round(tf, 5), "seconds": round(dt, 2), "slices": n}
+    del inp
+
+    if not args.no_configs:
+        configs = {}
+        for name in WORKLOAD_ORDER:
+            cw = WORKLOADS[name]
+            cinp, configs[name] = time_config(cw, args.config_calls, max(3, args.warmup // 2), poller,
+                                              args.clock_window / 2)
+            torch.cuda.empty_cache()
+            if not args.no_cpu and name != STEP_WORKLOAD:
+                tf, dt, n = cpu_oracle_sample(cw, cinp, CPU_SLICES[name], with_bwd=False)
+                cpu[name] = {"value": round(tf, 5), "seconds": round(dt, 2), "slices": n, "pass": "forward"}
+            del cinp
+        out["configs"] = configs
+
+        # fa_bwd_atomic (single pass, dQ by fp32 atomics) on the step's workload, as context.
+        _, q, k, v, do = device_inputs(w, with_do=True)
+        st = Step(w, q, k, v, do)
+        st.fwd()
+        per_a, _, _ = time_calls(st, [st.bwd_atomic], args.config_calls, 3)
+        out["bwd_atomic_dq"] = time_stats(per_a, bf, bwd_bytes(B, H, Hkv, N, N, d), clock)
+        out["bwd_atomic_dq"]["note"] = "fa_bwd_atomic on the step's workload (not in the timed step)"
+        del st, q, k, v, do
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        host = host_description()
+        s = cpu[STEP_WORKLOAD]
+        out["cpu_baseline"] = {
+            "value": s["value"], "unit": "TFLOPS", "cores": host["blas_threads"], "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of {s['slices']} of {B * H} (batch, head) slices of the step's "
+                      f"workload (N={N}, d={d}, causal), {s['seconds']:.1f} s wall, same causal-adjusted flop count; "
+                      "BLAS calls run on the threads counted in cores, the elementwise work on one",
+            **host,
+            "per_config": {k2: v2 for k2, v2 in cpu.items() if k2 != STEP_WORKLOAD},
+        }
     print(json.dumps(out), flush=True)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
-
-
-def copy_calibration(mib):
-    """dst.copy_(src) of `mib` MiB, three times: reads and writes exactly that
-    many bytes per launch."""
-    import torch
-    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": mib << 20}), flush=True)
-
-
-def bench_one(args):
-    """Time one named workload's pass (fwd or bwd); prints one JSON line."""
-    print(json.dumps(time_workload(WORKLOADS[args.workload], args.steps, args.warmup)), flush=True)
-
-
-def time_workload(w, steps, warmup):
-    """Median time of one named workload's pass (fwd or bwd), as a dict."""
-    inp, q, k, v, do = device_inputs(w, with_do=w.passes == "bwd")
-    step = Step(w, q, k, v, do if do is not None else q)
-    if w.passes == "bwd":
-        step.fwd()
-        calls, fl = [step.bwd], bwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
-        by = bwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim)
-    else:
-        calls, fl = [step.fwd], fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
-        eb = 4 if w.dtype == "f32" else 2
-        by = fwd_bytes(w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim, eb, eb)
-    per_step, _, _ = time_calls(step, calls, steps, warmup)
-    ms = float(np.median(per_step))
-    tf = fl / (ms * 1e-3) / 1e12
-    return {"workload": w.name, "ms": round(ms, 4), "ms_min": round(float(per_step.min()), 4),
-            "tflops": round(tf, 2), "pct_of_bf16_peak": round(100 * tf / MI355X_BF16_PEAK_TFLOPS, 2),
-            "gbps_algorithmic": round(by / (ms * 1e-3) / 1e9, 1),
-            "pct_of_hbm": round(100 * by / (ms * 1e-3) / 1e9 / MI355X_HBM_GBPS, 2)}
 
 
 if __name__ == "__main__":

@@ -1,6 +1,8 @@
-"""CPU tests of bench.py's host logic: the rocprofv3 summariser (kernel to
-entry-point mapping, copy calibration of the byte counters, the recorded
-traffic file) and the refusal of more than one GPU."""
+"""CPU tests of bench.py's host logic: the rocprofv3 summarisers (kernel to
+entry-point mapping, copy calibration of the byte counters, read bytes by
+request size, L2 hit rate, SQ counter ratios, the recorded profile file and
+its staleness check), the amd-smi clock parser, the timing statistics, and
+the refusal of more than one GPU."""
 
 import csv
 import json
@@ -58,32 +60,152 @@ def test_kernel_to_entry_point():
     assert bench._call_of("void fa::fwd_fp8_kernel<true, false>(fa::FwdArgs)") == "fa_fwd_fp8"
 
 
+FWD = "void fa::fwd_kernel<false, 128, true, false, 8, false, false>(fa::FwdArgs)"
+DKDV = "void fa::bwd_dkdv_kernel<128, true, false, false, false>(fa::BwdArgs)"
+DQ = "void fa::bwd_dq_kernel<128, true, false, 8, false>(fa::BwdArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
 def test_summarize_profiles_calibrates_and_records(tmp_path, capsys):
     prof = tmp_path / "prof"
     os.makedirs(prof / "trace")
     with open(prof / "trace" / "bench_kernel_stats.csv", "w", newline="") as fh:
         w = csv.writer(fh)
         w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
-        w.writerow(["void fa::fwd_kernel<false, 128, true, false, 4>(fa::FwdArgs)", 2, 400000, 200000, 40, 190000,
-                    210000, 1])
-        w.writerow(["void fa::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs)", 2, 600000, 300000, 60, 290000, 310000,
-                    1])
-    copy = "__amd_rocclr_copyBuffer"
+        w.writerow([FWD, 2, 400000, 200000, 30, 190000, 210000, 1])
+        w.writerow([DKDV, 2, 600000, 300000, 45, 290000, 310000, 1])
+        w.writerow([DQ, 2, 300000, 150000, 25, 140000, 160000, 1])
     # a 4 MiB copy: FETCH_SIZE reports half the bytes, WRITE_SIZE all of them
     _write_counters(str(prof / "fetch" / "bench_counter_collection.csv"), "FETCH_SIZE",
-                    {copy: [2048, 2048], "void fa::fwd_kernel<false, 128, true, false, 4>(fa::FwdArgs)": [100, 300],
-                     "void fa::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs)": [1000]})
+                    {COPY: [2048, 2048], FWD: [100, 300], DKDV: [1000], DQ: [500]})
     _write_counters(str(prof / "write" / "bench_counter_collection.csv"), "WRITE_SIZE",
-                    {copy: [4096], "void fa::fwd_kernel<false, 128, true, false, 4>(fa::FwdArgs)": [10, 10],
-                     "void fa::bwd_dkdv_kernel<128, true, false>(fa::BwdArgs)": [50]})
-    out = tmp_path / "traffic.json"
+                    {COPY: [4096], FWD: [10, 10], DKDV: [50], DQ: [25]})
+    # request counts by size: the dK/dV pass reads 10 x 128 B + 4 x 64 B + 2 x 32 B
+    rd = {COPY: {"TCC_EA0_RDREQ_sum": 8, "TCC_EA0_RDREQ_32B_sum": 0, "TCC_EA0_RDREQ_64B_sum": 0,
+                 "TCC_EA0_RDREQ_128B_sum": 8},
+          DKDV: {"TCC_EA0_RDREQ_sum": 16, "TCC_EA0_RDREQ_32B_sum": 2, "TCC_EA0_RDREQ_64B_sum": 4,
+                 "TCC_EA0_RDREQ_128B_sum": 10},
+          DQ: {"TCC_EA0_RDREQ_sum": 1, "TCC_EA0_RDREQ_32B_sum": 0, "TCC_EA0_RDREQ_64B_sum": 1,
+               "TCC_EA0_RDREQ_128B_sum": 0}}
+    _write_multi(str(prof / "rdreq" / "bench_counter_collection.csv"), rd)
+    tcc = {DKDV: {"TCC_HIT_sum": 30, "TCC_MISS_sum": 10, "TCC_EA0_RDREQ_DRAM_sum": 9},
+           DQ: {"TCC_HIT_sum": 5, "TCC_MISS_sum": 5, "TCC_EA0_RDREQ_DRAM_sum": 4}}
+    _write_multi(str(prof / "tcc" / "bench_counter_collection.csv"), tcc)
+    out = tmp_path / "profile.json"
     bench.summarize_profiles(str(prof), 4, out_path=str(out))
     text = capsys.readouterr().out
     assert "scale x2.0000" in text and "scale x1.0000" in text
+    assert "| 75.0% |" in text  # dK/dV L2 hit rate 30 / 40
     rec = json.loads(out.read_text())
     assert rec["kernel_sources_sha256"] == bench.csrc_sha256()
-    assert rec["fa_fwd"] == {"fetch_bytes": 200 * 1024 * 2, "write_bytes": 10 * 1024}
-    assert rec["fa_bwd"] == {"fetch_bytes": 1000 * 1024 * 2, "write_bytes": 50 * 1024}
+    assert rec["workload"] == bench.STEP_WORKLOAD
+    assert rec["fa_fwd"]["kernel_avg_us"] == 200.0
+    assert rec["fa_fwd"]["fetch_bytes"] == 200 * 1024 * 2 and rec["fa_fwd"]["write_bytes"] == 10 * 1024
+    # fa_bwd = both of its kernels, summed per launch
+    assert rec["fa_bwd"]["kernel_avg_us"] == 450.0
+    assert rec["fa_bwd"]["fetch_bytes"] == 1500 * 1024 * 2
+    assert rec["fa_bwd"]["write_bytes"] == 75 * 1024
+    assert rec["fa_bwd"]["read_bytes_by_request_size"] == 10 * 128 + 4 * 64 + 2 * 32 + 64
+    assert rec["fa_bwd"]["l2_hits"] == 35 and rec["fa_bwd"]["l2_misses"] == 15
+    assert rec["fa_bwd"]["dram_read_requests"] == 13
+    # the recorded profile is used only while the kernel sources are unchanged
+    assert bench.profile_record("fa_bwd", str(out))["kernel_avg_us"] == 450.0
+    stale = dict(rec, kernel_sources_sha256="0" * 64)
+    out.write_text(json.dumps(stale))
+    assert bench.profile_record("fa_bwd", str(out)) is None
+
+
+def _write_multi(path, per_kernel):
+    """One dispatch per kernel with several counters."""
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=FIELDS)
+        w.writeheader()
+        for d, (name, counters) in enumerate(per_kernel.items(), 1):
+            for c, v in counters.items():
+                w.writerow({"Correlation_Id": d, "Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": c,
+                            "Counter_Value": v})
+
+
+def test_summarize_pmc_reports_coexec_and_valu_busy(tmp_path, capsys):
+    path = tmp_path / "sq" / "bench_counter_collection.csv"
+    os.makedirs(path.parent)
+    fields = FIELDS + ["Start_Timestamp", "End_Timestamp"]
+    # 8 XCDs x 2000 cycles in 1000 ns: 2.0 GHz; MFMA busy on half of 1024 SIMDs x 2000 cycles
+    vals = {"GRBM_GUI_ACTIVE": 16000, "SQ_WAVES": 100, "SQ_INSTS_VALU": 800, "SQ_INSTS_MFMA": 200,
+            "SQ_INSTS_LDS": 300, "SQ_VALU_MFMA_BUSY_CYCLES": 1024000, "SQ_LDS_BANK_CONFLICT": 0,
+            "SQ_VALU_MFMA_COEXEC_CYCLES": 256000, "SQ_ACTIVE_INST_VALU": 128000}
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        for c, v in vals.items():
+            w.writerow({"Correlation_Id": 1, "Dispatch_Id": 1, "Kernel_Name": DKDV, "Counter_Name": c,
+                        "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": 1000})
+    bench.summarize_pmc(str(path.parent))
+    row = [line for line in capsys.readouterr().out.splitlines() if DKDV in line][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    # clock, MFMA busy, VALU busy (128000 / 256 CUs / 2000 cycles), co-exec share of MFMA busy
+    assert cells[4:8] == ["2.00", "50.0", "25.0", "25.0"]
+    assert cells[10] == "4.00"  # VALU per MFMA
+
+
+# `amd-smi metric -g 0 --clock --json` output as printed on an idle MI355X
+# (trimmed to two XCDs and one other clock domain).
+AMD_SMI_CLOCK = """{
+    "gpu_data": [
+        {
+            "gpu": 0,
+            "clock": {
+                "gfx_0": {"clk": {"value": 2399, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                          "max_clk": {"value": 2400, "unit": "MHz"}, "clk_locked": "DISABLED",
+                          "deep_sleep": "ENABLED"},
+                "gfx_1": {"clk": {"value": 1801, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                          "max_clk": {"value": 2400, "unit": "MHz"}, "clk_locked": "DISABLED",
+                          "deep_sleep": "ENABLED"},
+                "mem_0": {"clk": {"value": 2000, "unit": "MHz"}}
+            }
+        }
+    ]
+}"""
+
+
+def test_clock_parsing_and_window():
+    assert bench.read_amd_smi_clock(AMD_SMI_CLOCK) == [2399.0, 1801.0]
+    assert bench.read_amd_smi_clock("WARNING: low-power state\n" + AMD_SMI_CLOCK) == [2399.0, 1801.0]
+    assert bench.read_amd_smi_clock("") is None
+    assert bench.read_amd_smi_clock("Unable to get devices, driver not initialized") is None
+    assert bench.read_amd_smi_clock('{"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": "N/A"}}}]}') is None
+    samples = [(0.5, 2400.0, 2390.0, 2410.0), (1.5, 1900.0, 1800.0, 2000.0), (2.5, 1950.0, 1850.0, 1990.0),
+               (3.5, 1000.0, 990.0, 1010.0)]
+    w = bench.clock_window(samples, 1.0, 3.0)
+    assert w == {"median": 1925.0, "min_xcd": 1800.0, "max_xcd": 2000.0, "samples": 2}
+    assert bench.clock_window(samples, 10.0, 11.0) is None
+    # dense bf16 peak at the published 2.4 GHz, and scaled to a measured clock
+    assert abs(bench.peak_at_clock(2400.0) - 2516.58) < 0.01
+    assert abs(bench.peak_at_clock(1900.0) / bench.peak_at_clock(2400.0) - 1900 / 2400) < 1e-12
+
+
+def test_time_stats():
+    ms = [1.0] * 9 + [2.0]
+    s = bench.time_stats(ms, 2e9, 4e6, {"median": 1200.0})
+    assert s["calls"] == 10 and s["ms_median"] == 1.0 and s["ms_min"] == 1.0 and s["ms_mean"] == 1.1
+    assert s["ms_p90"] == 1.1
+    assert s["tflops"] == 2.0 and s["gbps_algorithmic"] == 4.0
+    assert s["clock_mhz"] == 1200.0
+    assert abs(s["pct_of_bf16_peak_at_clock"] - round(100 * 2.0 / bench.peak_at_clock(1200.0), 2)) < 1e-9
+    assert "clock_mhz" not in bench.time_stats(ms, 2e9, 4e6, None)
+
+
+def test_host_description():
+    h = bench.host_description()
+    assert h["logical_cpus"] >= 1 and h["blas_threads"] >= 1
+    assert isinstance(h["cpu_model"], str) and isinstance(h["blas"], str)
+
+
+def test_cpu_slices_cover_every_workload():
+    from exact_tiled_attention_28_amd.workloads import WORKLOADS
+    assert set(bench.CPU_SLICES) == set(WORKLOADS)
+    assert bench.STEP_WORKLOAD in WORKLOADS and WORKLOADS[bench.STEP_WORKLOAD].passes == "bwd"
 
 
 def test_more_than_one_gpu_is_refused():
