@@ -798,6 +798,299 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV pass with four independent wavefronts: bwd_dkdv4_kernel
+// ---------------------------------------------------------------------------
+//
+// The same K/V-outer loop (page 6.2, section 7.2) with a layout that needs no
+// exchange between wavefronts: a workgroup owns a 64-key block and each of its
+// four wavefronts owns 16 of those keys outright. With the 16x16x32 bf16
+// MFMA a wavefront forms S = Q K^T and dP = dO V^T for all 64 query rows of a
+// Q block against its 16 keys (one key per lane column, K and V rows in
+// registers as B operands), and accumulates dV^T += dO^T P and dK^T += Q^T dS
+// over the full head dimension (16 keys x D, 2 x D/16 fp32 per lane). The
+// only workgroup barrier per Q block protects the double-buffered Q/dO/L/D
+// tiles (4 x 64 rows + L/D: 33 KiB at d = 64), so several workgroups share a
+// CU and their wavefronts interleave matrix and vector work on each SIMD
+// independently. The 16x16 products read twice the operand bytes per flop of
+// the 32x32 ones, so the kernel serves d = 64, where it is the faster layout.
+//
+// 16x16x32 MFMA layouts (gfx950): A (16 x 32): lane l holds row l % 16 and 8
+// k values chosen by the lane group G = l / 16; B (32 x 16): column l % 16,
+// the same k set; C (16 x 16, 4 fp32): column l % 16, rows 4G + i. S comes out
+// with lane l holding key l % 16 for queries 16 mb + 4G + i (m-block mb); two
+// m-blocks (2t, 2t + 1) form the 8 k slots of the products' B operand, and the
+// A operands (dO^T, Q^T) are transpose reads of exactly those query rows.
+//
+// LDS rows use the swizzle dkdv4_swz, which keeps both operand reads free of
+// bank conflicts: ds_read_b128 of 16 consecutive rows at one chunk (a
+// bijection on row % 16), and ds_read_b64_tr_b16 of rows 8h .. 8h + 7 over an
+// aligned pair of chunks (the 8 rows move the pair to 8 different pairs).
+template <int ROW_CHUNKS>
+__device__ __forceinline__ int dkdv4_swz(int row) {
+  if constexpr (ROW_CHUNKS >= 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+  // 128-byte rows: the row parity picks the half of the 256-byte bank period.
+  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+template <int ROW_CHUNKS>
+__device__ __forceinline__ int dkdv4_off(int row, int byte_in_row) {
+  const int c = byte_in_row >> 4;
+  return row * (ROW_CHUNKS * 16) + (((c ^ dkdv4_swz<ROW_CHUNKS>(row)) << 4) | (byte_in_row & 15));
+}
+
+// C += A * B, 16x16 output, K = 32, bf16 operands, fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Dkdv4Tile {
+  static constexpr int NW = 4;
+  static constexpr int BKV = 64, BQ = 64;
+  static constexpr int ROWB = D * 2, RC = ROWB / 16;
+  static constexpr int QTILEB = BQ * ROWB;
+  static constexpr int QCPW = QTILEB / (1024 * NW);
+  static_assert(QTILEB % (1024 * NW) == 0, "tiles must split evenly");
+};
+
+template <int D, bool CAUSAL, bool GF32, bool VARLEN = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv4_kernel(BwdArgs a) {
+  using T = Dkdv4Tile<D>;
+  constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB, QCPW = T::QCPW;
+  constexpr int NK32 = D / 32, NDB = D / 16;  // 32-wide head-dim steps, 16-wide head-dim blocks
+
+  __shared__ __attribute__((aligned(16))) char sQ0[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sQ1[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sDO0[QTILEB];
+  __shared__ __attribute__((aligned(16))) char sDO1[QTILEB];
+  __shared__ __attribute__((aligned(16))) float sL0[BQ];
+  __shared__ __attribute__((aligned(16))) float sL1[BQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BQ];
+  __shared__ __attribute__((aligned(16))) float sD1[BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int G = lane >> 4;  // lane group of the 16x16x32 layouts
+  const int n16 = lane & 15;
+
+  const UnitItem ui = xcd_decode(blockIdx.x, a.B * a.Hkv);
+  const int b = ui.unit / a.Hkv;
+  const int hkv = ui.unit % a.Hkv;
+  const int kv0 = ui.item * BKV;
+  const int key = kv0 + 16 * w + n16;  // this lane's key
+
+  int Nq = a.Nq, Nk = a.Nk;
+  size_t kvhead;
+  int q_off = 0;
+  if constexpr (VARLEN) {
+    const SeqSpan sq = clamp_span(a.cu_q[b], a.cu_q[b + 1], a.total_q, a.Nq);
+    const SeqSpan sk = clamp_span(a.cu_k[b], a.cu_k[b + 1], a.total_k, a.Nk);
+    Nq = sq.len;
+    Nk = sk.len;
+    if (kv0 >= Nk) return;  // the whole key block lies past this sequence
+    q_off = sq.off;
+    kvhead = (size_t)hkv * a.total_k + sk.off;
+  } else {
+    kvhead = (size_t)(b * a.Hkv + hkv) * a.Nk;
+  }
+  auto q_base = [&](int hq) __attribute__((always_inline)) -> size_t {
+    if constexpr (VARLEN) return (size_t)hq * a.total_q + q_off;
+    return (size_t)(b * a.Hq + hq) * a.Nq;
+  };
+
+  // K and V rows of this lane's key as B operands: head-dim elements
+  // 32*kk + 8*G .. +7 (zero past the end of K/V).
+  bf16x8 kf[NK32], vf[NK32];
+  {
+    const bool ok = key < Nk;
+    const size_t row = (kvhead + (ok ? key : 0)) * ROWB;
+    const char* Kr = (const char*)a.k + row;
+    const char* Vr = (const char*)a.v + row;
+#pragma unroll
+    for (int kk = 0; kk < NK32; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (ok) {
+        x = *(const u32x4*)(Kr + (kk * 32 + 8 * G) * 2);
+        y = *(const u32x4*)(Vr + (kk * 32 + 8 * G) * 2);
+      }
+      kf[kk] = __builtin_bit_cast(bf16x8, x);
+      vf[kk] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+
+  // Per-lane LDS offsets: row reads (row n16 of a 16-row m-block, head-dim
+  // step kk) and transpose reads (rows 4G + n16/4 of a 32-row query step,
+  // columns of head-dim block db); other m-blocks and query steps are whole
+  // 16-row periods away.
+  int roff[NK32];
+#pragma unroll
+  for (int kk = 0; kk < NK32; ++kk) roff[kk] = dkdv4_off<RC>(n16, (kk * 32 + 8 * G) * 2);
+  int troff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) troff[db] = dkdv4_off<RC>(4 * G + (n16 >> 2), (db * 16 + 4 * (n16 & 3)) * 2);
+
+  f32x4 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dkacc[db] = f32x4{};
+    dvacc[db] = f32x4{};
+  }
+
+  const int n_qblk = ceil_div(Nq, BQ);
+  const int i_first = first_q_tile_for(kv0, BQ, CAUSAL);
+  const int n_i = n_qblk - i_first;
+  const int total = a.G * n_i;
+  const float c = a.c;
+  const float scale = a.scale;
+
+  // The next Q block's L and D are loaded into registers (wavefront 0) as
+  // its Q/dO tiles are issued and stored to LDS at the end of the current
+  // block.
+  float lr = 0.0f, dr = 0.0f;
+  bool lok = false;
+  auto issue_q = [&](int it, char* nQ, char* nDO) __attribute__((always_inline)) {
+    const int hm = it / n_i;
+    const int i = i_first + it % n_i;
+    const int hq = hkv * a.G + hm;
+    const size_t qhead = q_base(hq);
+    const int q0 = i * BQ;
+    if (tid < BQ) {
+      lok = q0 + tid < Nq;
+      const size_t r = qhead + q0 + (lok ? tid : 0);
+      lr = a.lse[r];
+      dr = a.dvec[r];
+    }
+    const char* Qb = uniform_ptr((const char*)a.q + (qhead + q0) * ROWB);
+    const char* Ob = uniform_ptr((const char*)a.dout + (qhead + q0) * ROWB);
+    const int last = Nq - 1 - q0;
+#pragma unroll
+    for (int u = 0; u < QCPW; ++u) {
+      const int cb = (w * QCPW + u) * 64;
+      const int idx = cb + lane;
+      const int row = idx / RC, pc = idx % RC;
+      const int lc = pc ^ dkdv4_swz<RC>(row);
+      unsigned off = (unsigned)(min(row, last) * ROWB + lc * 16);
+      asm volatile("" : "+v"(off));
+      load_lds_16(Qb + off, nQ + cb * 16);
+      load_lds_16(Ob + off, nDO + cb * 16);
+    }
+  };
+  auto store_ld = [&](float* nL, float* nD) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      nL[tid] = lok ? lr * kLog2e : INFINITY;
+      nD[tid] = lok ? dr : 0.0f;
+    }
+  };
+
+  if (total > 0) {
+    issue_q(0, sQ0, sDO0);
+    store_ld(sL0, sD0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // One Q block of 64 rows against this wavefront's 16 keys.
+  auto body = [&](auto mask_tag, int q0, const char* tQ, const char* tDO, const float* tL, const float* tD)
+                  __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // S = Q K^T and dP = dO V^T, m-block mb: queries 16 mb + 4G + i.
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      s[mb] = f32x4{};
+      dp[mb] = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < NK32; ++kk) {
+        s[mb] = mfma16_bf16(*(const bf16x8*)(tQ + mb * 16 * ROWB + roff[kk]), kf[kk], s[mb]);
+        dp[mb] = mfma16_bf16(*(const bf16x8*)(tDO + mb * 16 * ROWB + roff[kk]), vf[kk], dp[mb]);
+      }
+    }
+    // P = exp2(S c - L log2 e), dS = P o (dP - D). Masked: query
+    // q0 + 16 mb + 4G + i sees this lane's key iff 16 mb + i >= tq (no query
+    // if the key is past the end of K, every query without the causal mask).
+    const int tq = key >= Nk ? INT_MAX : (CAUSAL ? key - q0 - 4 * G : INT_MIN);
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const f32x4 lv = *(const f32x4*)(tL + 16 * mb + 4 * G);
+      const f32x4 dv = *(const f32x4*)(tD + 16 * mb + 4 * G);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = fast_exp2(fmaf(s[mb][i], c, -lv[i]));
+        if constexpr (MASK) p = (16 * mb + i >= tq) ? p : 0.0f;
+        pv[4 * mb + i] = p;
+        dsv[4 * mb + i] = p * (dp[mb][i] - dv[i]);
+      }
+    }
+    // Query step t: k slots 0-3 hold queries 32t + 4G + i, slots 4-7 hold
+    // 32t + 16 + 4G + i (m-blocks 2t and 2t + 1).
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pb = to_bf16x8(pv + 8 * t);
+      const bf16x8 sb = to_bf16x8(dsv + 8 * t);
+      const char* oT = tDO + 32 * t * ROWB;
+      const char* qT = tQ + 32 * t * ROWB;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(oT + troff[db]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(oT + 16 * ROWB + troff[db]));
+        dvacc[db] = mfma16_bf16(cat4(lo, hi), pb, dvacc[db]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(qT + troff[db]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(qT + 16 * ROWB + troff[db]));
+        dkacc[db] = mfma16_bf16(cat4(lo, hi), sb, dkacc[db]);
+      }
+    }
+  };
+
+  auto block = [&](int it, const char* tQ, const char* tDO, const float* tL, const float* tD, char* nQ, char* nDO,
+                   float* nL, float* nD) __attribute__((always_inline)) {
+    const int i = i_first + it % n_i;
+    const int q0 = i * BQ;
+    const bool has_next = it + 1 < total;
+    if (has_next) issue_q(it + 1, nQ, nDO);
+    // Skipped when all of this wavefront's keys lie after all the block's
+    // queries; masked when some key lies after some query or past the end.
+    const bool active = !CAUSAL || kv0 + 16 * w <= q0 + BQ - 1;
+    if (active) {
+      const bool need_mask = (CAUSAL && kv0 + 16 * w + 15 > q0) || (kv0 + 16 * w + 16 > Nk);
+      if (need_mask)
+        body(std::true_type{}, q0, tQ, tDO, tL, tD);
+      else
+        body(std::false_type{}, q0, tQ, tDO, tL, tD);
+    }
+    if (has_next) store_ld(nL, nD);
+    wait_vmem();
+    __syncthreads();
+  };
+  for (int it = 0; it < total; it += 2) {
+    block(it, sQ0, sDO0, sL0, sD0, sQ1, sDO1, sL1, sD1);
+    if (it + 1 >= total) break;
+    block(it + 1, sQ1, sDO1, sL1, sD1, sQ0, sDO0, sL0, sD0);
+  }
+
+  // ---- epilogue: dK = scale * dK^T, dV = dV^T: head-dim 16 db + 4G + i ----
+  if (key < Nk) {
+    const size_t rowoff = (kvhead + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d0 = db * 16 + 4 * G;
+      const f32x4 kv = {scale * dkacc[db][0], scale * dkacc[db][1], scale * dkacc[db][2], scale * dkacc[db][3]};
+      const f32x4 vv = dvacc[db];
+      if constexpr (GF32) {
+        *(f32x4*)((float*)a.dk + rowoff + d0) = kv;
+        *(f32x4*)((float*)a.dv + rowoff + d0) = vv;
+      } else {
+        *(bf16x4*)((__bf16*)a.dk + rowoff + d0) = __builtin_convertvector(kv, bf16x4);
+        *(bf16x4*)((__bf16*)a.dv + rowoff + d0) = __builtin_convertvector(vv, bf16x4);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // second pass: dQ_i = scale * sum_j dS_ij K_j, Q-outer like the forward
 // ---------------------------------------------------------------------------
 //
@@ -1096,8 +1389,18 @@ static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The dK/dV pass: at d = 64 the four-wavefront kernel (2-16 % faster on
+// MI355X over causal, GQA and non-causal shapes up to 8K keys, level at 16K
+// non-causal), else, and with HILO, the eight-wavefront kernel with the P/dS
+// exchange (at d = 128 the four-wavefront layout reads 1.6x the LDS bytes
+// per flop and measured between -7 % and +4 % against it).
 template <int D, bool CAUSAL, bool GF32, bool HILO>
 static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  if constexpr (!HILO && D == 64) {
+    const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, Dkdv4Tile<D>::BKV);
+    hipLaunchKernelGGL((bwd_dkdv4_kernel<D, CAUSAL, GF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   using T = DkdvTile<D, HILO>;
   auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, false, HILO>;
   const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, T::BKV);
@@ -1173,6 +1476,12 @@ static hipError_t launch_bwd_varlen_h(const BwdArgs& a0, bool o_f32, hipStream_t
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+  }
+  if constexpr (!HILO && D == 64) {
+    const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, Dkdv4Tile<D>::BKV);
+    if (blocks > 0)
+      hipLaunchKernelGGL((bwd_dkdv4_kernel<D, CAUSAL, GF32, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
   }
   using T = DkdvTile<D, HILO>;
   auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, true, HILO>;

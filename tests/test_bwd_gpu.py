@@ -196,21 +196,22 @@ def test_bwd_with_bf16_o(case):
     check_flat(dQ, dK, dV, dQr, dKr, dVr, f"{_cid(case)} bf16 O")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("hilo", [False, True], ids=["bf16", "hilo"])
-def test_bwd_nan_in_one_q_row(hilo):
+def test_bwd_nan_in_one_q_row(hilo, d):
     """A NaN in query row i of one head (causal, the K/V head shared by two
     query heads). The outputs that depend on that row become NaN: O_i, L_i,
     D_i, dQ_i, and dV_j, dK_j of every key j <= i it sees. The K/V-outer pass
-    forms dK_j = s sum_i dS_ij Q_i over aligned blocks of 32 query rows, so a
-    NaN in Q_i (and in D_i, through dS_ij = P_ij (dP_ij - D_i) with P_ij = 0)
-    also reaches dK_j for the keys after i up to the end of i's 32-row
-    block, j <= 32 floor(i / 32) + 31, which do not depend on it. Every other
-    output is finite and matches the oracle evaluated with the row set to
-    zero."""
+    forms dK_j = s sum_i dS_ij Q_i over aligned blocks of query rows (64 rows
+    at head dim 64 with bf16 P and dS, else 32 rows), so a NaN in Q_i (and in
+    D_i, through dS_ij = P_ij (dP_ij - D_i) with P_ij = 0) also reaches dK_j
+    for the keys after i up to the end of i's block, j <= 64 floor(i / 64) + 63
+    (j <= 32 floor(i / 32) + 31), which do not depend on it. Every other output
+    is finite and matches the oracle evaluated with the row set to zero."""
     import torch
-    B, Hq, Hkv, N, d = 1, 2, 1, 300, 128
+    B, Hq, Hkv, N = 1, 2, 1, 300
     i = 77
-    announce(f"bwd NaN Q row hilo={hilo}")
+    announce(f"bwd NaN Q row hilo={hilo} d={d}")
     inp = gen(71, B, Hq, Hkv, N, N, d, with_do=True)
     clean_q = inp.q.copy()
     clean_q[0, 1, i] = 0.0
@@ -228,7 +229,8 @@ def test_bwd_nan_in_one_q_row(hilo):
     dv_nan = np.zeros((B, Hkv, N), dtype=bool)
     dv_nan[0, 0] = keys <= i
     dk_nan = np.zeros((B, Hkv, N), dtype=bool)
-    dk_nan[0, 0] = keys <= 32 * (i // 32) + 31
+    blk = 64 if (d == 64 and not hilo) else 32
+    dk_nan[0, 0] = keys <= blk * (i // blk) + blk - 1
     assert np.array_equal(np.isnan(Dv), rows_nan)
     assert np.array_equal(np.isnan(dQ).any(axis=-1), rows_nan) and np.all(np.isnan(dQ[rows_nan]))
     assert np.array_equal(np.isnan(dV).any(axis=-1), dv_nan) and np.all(np.isnan(dV[dv_nan]))
