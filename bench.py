@@ -99,6 +99,9 @@ def parse(argv=None):
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
                    help="summarise rocprofv3 output under DIR/{trace,fetch,write,rdreq,tcc} (no GPU needed) and "
                         "record per-launch durations and HBM bytes for the current kernel sources")
+    p.add_argument("--profile-out", default=PROFILE_JSON, metavar="PATH",
+                   help="where --summarize-profiles records the per-launch figures (default: the step's record "
+                        "under profiles/, which the benchmark line reads)")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR",
                    help="summarise a rocprofv3 --pmc run of the SQ counters under DIR (no GPU needed)")
     p.add_argument("--calibration-mib", type=int, default=256, help="copy size used by the counter runs")
@@ -766,7 +769,7 @@ def summarize_profiles(prof_dir, calib_mib, out_path=None):
             rb = 32 * n32 + 64 * n64 + 128 * n128
             fs = fetch_scaled.get(name)
             print(f"| `{name}` | {call} | {n:.0f} | {n32:.0f} | {n64:.0f} | {n128:.0f} | "
-                  f"{n - n32 - n64 - n128:.0f} | {rb / 1e6:.0f} | {'-' if fs is None else f'{fs / 1e6:.0f}'} |")
+                  f"{max(0, round(n - n32 - n64 - n128))} | {rb / 1e6:.0f} | {'-' if fs is None else f'{fs / 1e6:.0f}'} |")
             if call != "copy":
                 c = per_call.setdefault(call, {})
                 c["read_bytes_by_request_size"] = c.get("read_bytes_by_request_size", 0) + int(round(rb))
@@ -889,7 +892,7 @@ def main():
     if args.poll_clock is not None:
         return poll_clock_main(args.poll_clock)
     if args.summarize_profiles:
-        return summarize_profiles(args.summarize_profiles, args.calibration_mib)
+        return summarize_profiles(args.summarize_profiles, args.calibration_mib, args.profile_out)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
     if args.gpus != 1:
