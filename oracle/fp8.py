@@ -21,10 +21,21 @@ readings used here are:
 * scaling: one power-of-two scale 2^e per block of 64 rows of a (batch,
   head), the smallest with max|y| <= 448 * 2^e (so y / 2^e is exact and
   never saturates), kept a normal float32 number: e >= -126, and e = 0
-  for an all-zero block.
+  for an all-zero block; or, "per tensor", one such scale for the whole
+  array (the page's baseline of standard FP8 attention, whose scaling the
+  page does not state);
+* V: quantized the same way but never transformed (the transform is only
+  free for Q and K, whose product it leaves unchanged);
+* P: the second product can take the probabilities in FP8 too. Reading:
+  with the row maximum m, P~ = exp(S - m) lies in (0, 1], and P~ * 2^8 is
+  quantized with the same rounding (a fixed power-of-two scale, so the
+  largest probability is exactly 1 and values down to 2^-14 keep E4M3's
+  3 mantissa bits); the row sum l = sum P~ stays exact (fp64 here), so
+  O = (fp8(P~) V) / l and L = m + ln l.
 
 The attention itself is then the plain fp64 definition (oracle.attention) on
-the dequantized values decode(code) * 2^e.
+the dequantized values decode(code) * 2^e, or, with P in FP8, the same steps
+written out with the quantized P~ in the second product.
 """
 
 from __future__ import annotations
@@ -108,19 +119,21 @@ def block_scale_exponent(amax):
     return e
 
 
-def quantize(x, signs=None):
+def quantize(x, signs=None, per_tensor=False):
     """Codes [..., N, d] (uint8) and block scales [..., ceil(N/64)] (float64
-    powers of two) of x [..., N, d] (values exactly representable in fp32)."""
+    powers of two) of x [..., N, d] (values exactly representable in fp32).
+    per_tensor: one scale for the whole array (repeated in every block)."""
     x = np.asarray(x, dtype=np.float32)
     y = hadamard_rows(x, signs) if signs is not None else x.copy()
     N = y.shape[-2]
     nb = -(-N // BLOCK_ROWS)
     codes = np.empty(y.shape, dtype=np.uint8)
     scales = np.empty(y.shape[:-2] + (nb,))
+    e_all = block_scale_exponent(np.max(np.abs(y))) if per_tensor and y.size else None
     for idx in np.ndindex(*y.shape[:-2]):
         for j in range(nb):
             blk = y[idx][j * BLOCK_ROWS:(j + 1) * BLOCK_ROWS].astype(np.float64)
-            e = block_scale_exponent(np.max(np.abs(blk)))
+            e = e_all if per_tensor else block_scale_exponent(np.max(np.abs(blk)))
             scales[idx + (j,)] = 2.0 ** e
             codes[idx][j * BLOCK_ROWS:(j + 1) * BLOCK_ROWS] = e4m3_encode(blk / 2.0 ** e)
     return codes, scales
@@ -134,9 +147,53 @@ def dequantize(codes, scales):
     return vals * rep[..., None]
 
 
-def forward_fp8(q, k, v, scale, causal, signs=None):
-    """The FP8 forward: quantize Q and K (same signs), then the plain fp64
-    attention of the dequantized Q, K with V as given. Returns (O, L)."""
-    qc, qs = quantize(q, signs)
-    kc, ks = quantize(k, signs)
-    return _forward(dequantize(qc, qs), dequantize(kc, ks), v, scale, causal)
+P_SCALE = 2.0 ** 8  # fixed scale of the probabilities' FP8 codes
+
+
+def quantize_probs(p):
+    """fp8(P~): each probability in [0, 1] as the E4M3 value of P~ * 2^8,
+    divided back by 2^8 (float64)."""
+    p = np.asarray(p, dtype=np.float64)
+    if np.any(p < 0) or np.any(p > 1):
+        raise ValueError("probabilities must lie in [0, 1]")
+    return e4m3_decode(e4m3_encode(p * P_SCALE)) / P_SCALE
+
+
+def forward_probs_fp8(q, k, v, scale, causal):
+    """Attention with the probabilities rounded to FP8 in the second
+    product: per (batch, query head), S = s Q K^T (causal mask -inf),
+    m = rowmax S, P~ = exp(S - m), l = sum P~, O = (fp8(P~) V) / l,
+    L = m + ln l. q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]; float64 results."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, Hq, Nq, d = q.shape
+    G = Hq // k.shape[1]
+    Nk = k.shape[2]
+    O = np.empty((B, Hq, Nq, v.shape[-1]))
+    L = np.empty((B, Hq, Nq))
+    cols = np.arange(Nk)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for a in range(0, Nq, 256):
+                rows = np.arange(a, min(Nq, a + 256))
+                S = float(scale) * (q[b, h, rows] @ k[b, g].T)
+                if causal:
+                    S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+                m = S.max(axis=1)
+                Pt = np.exp(S - m[:, None])
+                ell = Pt.sum(axis=1)
+                O[b, h, rows] = (quantize_probs(Pt) @ v[b, g]) / ell[:, None]
+                L[b, h, rows] = m + np.log(ell)
+    return O, L
+
+
+def forward_fp8(q, k, v, scale, causal, signs=None, per_tensor=False, v_fp8=False, p_fp8=False):
+    """The FP8 forward: quantize Q and K (same signs; 64-row block scales, or
+    one scale per tensor), optionally V (never transformed) and P, then the
+    fp64 attention of the dequantized values. Returns (O, L)."""
+    qc, qs = quantize(q, signs, per_tensor)
+    kc, ks = quantize(k, signs, per_tensor)
+    vv = dequantize(*quantize(v, None, per_tensor)) if v_fp8 else v
+    if p_fp8:
+        return forward_probs_fp8(dequantize(qc, qs), dequantize(kc, ks), vv, scale, causal)
+    return _forward(dequantize(qc, qs), dequantize(kc, ks), vv, scale, causal)
