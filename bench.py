@@ -96,6 +96,8 @@ def parse(argv=None):
                    help="time fa_fwd_persistent beside fa_fwd (forward workload B8 H16 N2048, or --workload)")
     p.add_argument("--fp8", action="store_true",
                    help="time fa_quantize_fp8 (Q and K) + fa_fwd_fp8 beside fa_fwd (B8 H16 N2048, or --workload)")
+    p.add_argument("--fp8-d64", action="store_true",
+                   help="with --fp8: the head-dim-64 shape B8 H32 N2048 causal (seed 2) instead")
     p.add_argument("--summarize-profiles", default=None, metavar="DIR",
                    help="summarise rocprofv3 output under DIR/{trace,fetch,write,rdreq,tcc} (no GPU needed) and "
                         "record per-launch durations and HBM bytes for the current kernel sources")
@@ -546,9 +548,13 @@ def bench_fp8(args):
     and O = P V at the bf16 peak: half of the flops each."""
     import torch
     from exact_tiled_attention_28_amd.inputs import make_signs
-    w = WORKLOADS[args.workload or DEFAULT_FWD]
-    if w.passes != "fwd" or w.head_dim != 128 or w.dtype != "bf16":
-        raise SystemExit(f"--fp8 needs a bf16 forward workload with head_dim 128, not {w.name}")
+    from exact_tiled_attention_28_amd.workloads import Workload
+    if args.fp8_d64:
+        w = Workload("fwd_bf16_causal_b8_h32_n2048_d64", 8, 32, 32, 2048, 64, True, "bf16", "fwd", 2)
+    else:
+        w = WORKLOADS[args.workload or DEFAULT_FWD]
+    if w.passes != "fwd" or w.dtype != "bf16":
+        raise SystemExit(f"--fp8 needs a bf16 forward workload, not {w.name}")
     _, q, k, v, _ = device_inputs(w, with_do=False)
     step = Step(w, q, k, v, q)
     signs = torch.from_numpy(make_signs(w.seed, w.head_dim)).cuda()

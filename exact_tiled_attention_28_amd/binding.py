@@ -331,7 +331,7 @@ def quantize_fp8(x, signs=None, codes=None, scales=None, stream=None):
 def forward_fp8(q_codes, q_scales, k_codes, k_scales, v, scale, causal, out_dtype=None, o=None, lse=None,
                 stream=None):
     """O, L of the FP8 forward from codes and block scales written by
-    quantize_fp8 (same signs for Q and K); v [B,Hkv,Nk,128] bf16."""
+    quantize_fp8 (same signs for Q and K); v [B,Hkv,Nk,d] bf16, d = 64 or 128."""
     import torch
     B, Hq, Nq, d = q_codes.shape
     Hkv, Nk = k_codes.shape[1], k_codes.shape[2]

@@ -311,7 +311,7 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes, 
     return fail(FA_ERR_INVALID_ARGUMENT, q_scales == nullptr ? "q_scales is NULL" : "k_scales is NULL");
   if ((reinterpret_cast<uintptr_t>(q_scales) & 3u) || (reinterpret_cast<uintptr_t>(k_scales) & 3u))
     return fail(FA_ERR_INVALID_ARGUMENT, "q_scales / k_scales must be 4-byte aligned");
-  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward supports head_dim 128");
+
   fa::FwdArgs a{};
   a.q = q_codes;
   a.k = k_codes;
@@ -328,7 +328,7 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes, 
   a.neg = scale < 0.0f;
   a.q_scales = q_scales;
   a.k_scales = k_scales;
-  hipError_t e = fa::launch_fwd_fp8(a, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd_fp8(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
   return hip_status(e, "fa_fwd_fp8 launch");
 }
 

@@ -76,8 +76,8 @@ __device__ __forceinline__ bf16x8 bf16_residual8(const float* x, bf16x8 hi) {
   return to_bf16x8(r);
 }
 
-// LDS tiles hold rows of ROW_CHUNKS 16-byte chunks (ROW_CHUNKS >= 8, rows a
-// multiple of 128 bytes). Chunk c of row r is stored at chunk position
+// LDS tiles hold rows of ROW_CHUNKS 16-byte chunks (ROW_CHUNKS = 4, or >= 8
+// with rows a multiple of 128 bytes). Chunk c of row r is stored at chunk position
 // c ^ swz(r). The gfx950 LDS serves 64 banks of 4 bytes (256 bytes) per
 // cycle; swz is chosen so that the two operand reads of the kernels touch
 // 64 distinct banks in every cycle:
@@ -92,13 +92,18 @@ __device__ __forceinline__ bf16x8 bf16_residual8(const float* x, bf16x8 hi) {
 // row parity selects its half; swz(r) = 4*((r/2)%2) + (r/4)%4 is a bijection
 // on bits 1-3 of r, and rows r and r+2 of any 4 aligned rows (same parity)
 // get different blocks.
+// 64-byte rows (4 chunks, the FP8 K tile at d = 64, read only by
+// ds_read_b128 of 16 consecutive rows at one logical chunk): four rows share
+// a bank period, row % 4 picks the quarter, and swz(r) = (r/4) % 4 gives the
+// four rows of one quarter four different chunks.
 // swz depends only on r % 16, so moving by whole 16-row steps keeps every
 // lane's chunk position; all kernels step their per-lane offsets by multiples
 // of 16 rows.
 template <int ROW_CHUNKS>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(ROW_CHUNKS >= 8, "rows of at least 128 bytes");
+  static_assert(ROW_CHUNKS == 4 || ROW_CHUNKS >= 8, "rows of 64 or at least 128 bytes");
   if constexpr (ROW_CHUNKS >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if constexpr (ROW_CHUNKS == 4) return (row >> 2) & 3;
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

@@ -175,10 +175,10 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const 
 }
 
 // ---------------------------------------------------------------------------
-// FP8 forward, d = 128: fwd_kernel's tiling (4 wavefronts x 32 query rows,
-// 64-key tiles, K/V double-buffered in LDS by HBM -> LDS loads) with the K
-// tile held as e4m3 codes (8 KiB, rows of 128 bytes) and S^T = K Q^T formed
-// by two 32x32x64 FP8 MFMAs per 32-key block. For those MFMAs a lane of
+// FP8 forward, d = 64 and 128: fwd_kernel's tiling (4 wavefronts x 32 query
+// rows, 64-key tiles, K/V in LDS filled by HBM -> LDS loads) with the K tile
+// held as e4m3 codes (d bytes per row: 8 KiB at d = 128, 4 KiB at 64) and
+// S^T = K Q^T formed by d / 64 32x32x64 FP8 MFMAs per 32-key block. For those MFMAs a lane of
 // half-wave g supplies, in both operands, the 32 codes of head-dim range
 // [64 ks + 32 g, +32) of its key (A) or query (B) row: A and B then put the
 // same channel in the same slot, and the output has the 32x32 layout of the
@@ -187,14 +187,15 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const 
 // scores of a tile are scaled by one scalar s_q s_k, folded into the base-2
 // softmax constant.
 // ---------------------------------------------------------------------------
-template <bool CAUSAL, bool OUTF32>
+template <int D, bool CAUSAL, bool OUTF32>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_fp8_kernel(FwdArgs a) {
-  constexpr int D = 128, NW = 4, BR = 128, BC = 64, NKB = 2, NKS = D / 64, NDB = D / 32;
+  constexpr int NW = 4, BR = 128, BC = 64, NKB = 2, NKS = D / 64, NDB = D / 32;
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
   constexpr int KROWB = D, KRC = KROWB / 16, KTILEB = BC * KROWB, KCPW = KTILEB / (1024 * NW);  // fp8 K tile
   constexpr int VROWB = D * 2, VRC = VROWB / 16, VTILEB = BC * VROWB, VCPW = VTILEB / (1024 * NW);  // bf16 V
   static_assert(KTILEB % (1024 * NW) == 0 && VTILEB % (1024 * NW) == 0, "tiles must split into whole wave loads");
 
-  // Three K buffers and two V buffers (56 KiB): K_j is fetched two steps
+  // Three K buffers and two V buffers (56 KiB at d = 128): K_j is fetched two steps
   // before its scores, V_j one step before its product. Separate objects, so
   // that the compiler can tell the prefetch into one from reads of another.
   __shared__ __attribute__((aligned(16))) char sK0[KTILEB];
@@ -485,21 +486,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-hipError_t launch_fwd_fp8(const FwdArgs& a0, bool causal, bool out_f32, hipStream_t s) {
+template <int D>
+static void launch_fwd_fp8_d(const FwdArgs& a, long long blocks, bool causal, bool out_f32, hipStream_t s) {
+  if (causal) {
+    if (out_f32)
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else {
+    if (out_f32)
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  }
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a0, int head_dim, bool causal, bool out_f32, hipStream_t s) {
   FwdArgs a = a0;
   a.n_q_tiles = ceil_div(a.Nq, 128);
   const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
-  if (causal) {
-    if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((fwd_fp8_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  } else {
-    if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((fwd_fp8_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  }
+  if (head_dim == 64)
+    launch_fwd_fp8_d<64>(a, blocks, causal, out_f32, s);
+  else
+    launch_fwd_fp8_d<128>(a, blocks, causal, out_f32, s);
   return hipGetLastError();
 }
 

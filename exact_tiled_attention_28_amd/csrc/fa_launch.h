@@ -61,7 +61,7 @@ hipError_t launch_fwd_varlen(const FwdArgs& a, int head_dim, bool causal, bool o
 hipError_t launch_fwd_persistent(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
                                int N, int head_dim, hipStream_t s);
-hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, bool out_f32, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
 // fa_bwd_noalloc keeps D in a static device array of this many fp32 rows
 // (16 MiB per device); bwd_noalloc_scratch returns its device address on the
 // current device (looked up once per device, with hipGetSymbolAddress).

@@ -278,10 +278,10 @@ size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen);
  * Q and K), S = scale * (Q_codes 2^e_q)(K_codes 2^e_k)^T by FP8 matrix cores
  * (fp32 accumulate, one block scale pair per 64 x 64 score tile), then the
  * online softmax and O = P V exactly as fa_fwd (P rounded to bf16, V bf16).
- *   q_codes [B][Hq][Nq][128], k_codes [B][Hkv][Nk][128] uint8, 16-byte aligned
+ *   q_codes [B][Hq][Nq][d], k_codes [B][Hkv][Nk][d] uint8, 16-byte aligned
  *   q_scales [B][Hq][ceil(Nq/64)], k_scales [B][Hkv][ceil(Nk/64)] fp32
- *   v [B][Hkv][Nk][128] bf16; o, lse, scale, causal, out_dtype as in fa_fwd.
- * head_dim must be 128 (else FA_ERR_UNSUPPORTED).
+ *   v [B][Hkv][Nk][d] bf16; o, lse, scale, causal, out_dtype as in fa_fwd.
+ * head_dim (d) 64 or 128 (else FA_ERR_UNSUPPORTED).
  */
 int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes,
                const float* k_scales, const void* v, void* o, float* lse,

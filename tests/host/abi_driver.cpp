@@ -129,6 +129,8 @@ int main() {
          FA_ERR_INVALID_ARGUMENT);
   EXPECT(fa_fp8_scales_count(INT_MAX, INT_MAX, INT_MAX) > 0);
   EXPECT(fa_fwd_fp8(P, (const float*)P, P, (const float*)P, P, P, (float*)P, 1, 2, 1, 64, 64, 64, 0.1f, 0,
+                    FA_DTYPE_BF16, nullptr) == FA_OK);
+  EXPECT(fa_fwd_fp8(P, (const float*)P, P, (const float*)P, P, P, (float*)P, 1, 2, 1, 64, 64, 96, 0.1f, 0,
                     FA_DTYPE_BF16, nullptr) == FA_ERR_UNSUPPORTED);
   EXPECT(fa_fwd_persistent(P, P, P, P, (float*)P, (int*)P, 1, 2, 1, 64, 64, 128, 0.1f, 1, FA_DTYPE_BF16,
                            FA_DTYPE_BF16, nullptr) == FA_OK);

@@ -45,7 +45,7 @@ hipError_t launch_quantize_fp8(const void*, void*, float*, const signed char*, i
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_fwd_fp8(const FwdArgs& a, bool, bool, hipStream_t) {
+hipError_t launch_fwd_fp8(const FwdArgs& a, int, bool, bool, hipStream_t) {
   g_last_fwd = a;
   ++g_launches;
   return hipSuccess;

@@ -301,7 +301,7 @@ def test_quantize_fp8_argument_errors(lib, kw, code, text):
     (dict(causal=1, seqlen_k=17), UNSUP, "seqlen_q == seqlen_k"),
     (dict(out_dtype=9), INVALID, "FA_DTYPE"),
     (dict(scale=float("inf")), INVALID, "scale must be finite"),
-    (dict(head_dim=64), UNSUP, "head_dim 128"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
 ])
 def test_fwd_fp8_argument_errors(lib, kw, code, text):
     assert fwd_fp8(**kw) == code

@@ -145,18 +145,27 @@ FWD_CASES = [
     (1, 1, 1, 1100, 1100, True, True, 0, None),
     (1, 2, 2, 100, 448, False, False, 0, None),
 ]
+# head dim 64 (one FP8 product per 32-key block, 64-byte K rows)
+FWD_CASES_D64 = [
+    (1, 4, 2, 300, 300, True, True, 4, None),
+    (2, 2, 2, 130, 257, False, False, 0, None),
+    (1, 2, 1, 1, 1, True, True, 0, None),
+    (1, 2, 2, 200, 200, True, True, 2, -0.1),
+    (1, 1, 1, 1100, 1100, True, True, 0, None),
+    (1, 2, 1, 200, 1000, False, True, 0, None),
+]
+FWD_CASES_ALL = [c + (128,) for c in FWD_CASES] + [c + (64,) for c in FWD_CASES_D64]
 
 
 def _fwd_id(c):
     return f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}{'c' if c[5] else 'n'}{'s' if c[6] else ''}o{c[7]}" + \
-        ("" if c[8] is None else f"sc{c[8]}")
+        ("" if c[8] is None else f"sc{c[8]}") + f"d{c[9]}"
 
 
-@pytest.mark.parametrize("case", FWD_CASES, ids=[_fwd_id(c) for c in FWD_CASES])
+@pytest.mark.parametrize("case", FWD_CASES_ALL, ids=[_fwd_id(c) for c in FWD_CASES_ALL])
 def test_fwd_fp8_parity(case):
     import torch
-    B, Hq, Hkv, Nq, Nk, causal, with_signs, outl, scale = case
-    d = 128
+    B, Hq, Hkv, Nq, Nk, causal, with_signs, outl, scale, d = case
     scale = float(np.float32(1 / np.sqrt(d))) if scale is None else scale
     announce(f"fa_fwd_fp8 {_fwd_id(case)}")
     inp = gen(31 + Nq + Nk, B, Hq, Hkv, Nq, Nk, d, outliers=outl)
