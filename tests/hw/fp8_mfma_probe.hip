@@ -51,3 +51,25 @@ extern "C" int fp8_dot_probe(const void* cases, float* out, int n, void* stream)
 }
 
 extern "C" int fp8_dot_probe_case_bytes(void) { return (int)sizeof(ProbeCase); }
+
+// Converts n fp32 values (n a multiple of 4) to e4m3 codes with the pair
+// conversion the FP8 forward uses for P (v_cvt_pk_fp8_f32, round to nearest
+// even): four values per thread, packed into one 32-bit word as bytes 0-3.
+__global__ void __launch_bounds__(256) fp8_cvt_kernel(const float* __restrict__ in, unsigned* __restrict__ out,
+                                                      int nwords) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= nwords) return;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(in[4 * t], in[4 * t + 1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(in[4 * t + 2], in[4 * t + 3], w, true);
+  out[t] = (unsigned)w;
+}
+
+// in: device float[n], out: device uint8[n] (n a multiple of 4). Returns 0
+// or the HIP error code of the launch.
+extern "C" int fp8_cvt_probe(const float* in, void* out, int n, void* stream) {
+  if (n <= 0 || (n & 3)) return n == 0 ? 0 : -1;
+  const int nwords = n / 4;
+  hipLaunchKernelGGL(fp8_cvt_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, (hipStream_t)stream, in,
+                     (unsigned*)out, nwords);
+  return (int)hipGetLastError();
+}

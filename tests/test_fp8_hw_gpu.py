@@ -96,3 +96,36 @@ def test_fp8_instruction_error_is_within_the_window_bound():
     for k in range(1, 13):
         assert got[k - 1] == 1.0 + 2.0 ** -k
     assert got[20] == 1.0 + 2.0 ** -18 and got[21] == 2.0 ** 20 + 1
+
+
+def test_cvt_pk_fp8_rounds_like_the_e4m3_definition():
+    # v_cvt_pk_fp8_f32 (which the FP8 forward uses to pack P) against the
+    # oracle's E4M3 encoding on [0, 448]: every value, every midpoint between
+    # neighbours (ties to even), the fp32 neighbours of each midpoint, the
+    # subnormal range and random values; bit-exact.
+    import torch
+    lib = ctypes.CDLL(LIB)
+    lib.fp8_cvt_probe.restype = ctypes.c_int
+    lib.fp8_cvt_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    from oracle.fp8 import e4m3_encode
+    vals = e4m3_decode(np.arange(0x7F, dtype=np.uint8))  # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([vals, mids]).astype(np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(0)), np.nextafter(x, np.float32(448))])
+    rng = np.random.default_rng(3)
+    x = np.concatenate([x, rng.uniform(0, 448, 4000).astype(np.float32),
+                        (rng.uniform(0, 2.0 ** -5, 4000)).astype(np.float32),
+                        np.exp2(rng.uniform(-14, 8, 4000)).astype(np.float32)])
+    x = np.clip(x, 0, 448).astype(np.float32)
+    x = np.concatenate([x, -x])
+    x = np.concatenate([x, np.zeros((-len(x)) % 4, dtype=np.float32)])
+    announce(f"v_cvt_pk_fp8_f32 on {len(x)} values")
+    xin = torch.from_numpy(x).cuda()
+    out = torch.empty(len(x), dtype=torch.uint8, device="cuda")
+    rc = lib.fp8_cvt_probe(xin.data_ptr(), out.data_ptr(), len(x), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    got = out.cpu().numpy()
+    want = e4m3_encode(x.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, e.g. x={x[bad[:5]]} got={got[bad[:5]]} want={want[bad[:5]]}"
