@@ -187,6 +187,49 @@ def forward_probs_fp8(q, k, v, scale, causal):
     return O, L
 
 
+def forward_probs_fp8_online(q, k, v, scale, causal, tile=64, quant=None):
+    """P in FP8 the way a tiled forward forms it: against the running row
+    maximum of the key tiles seen so far (online softmax, page "6.2
+    FlashAttention V2 chi tiết", section 6.1), so the rounding is applied to
+    exp(S_j - m_j) of each tile j, not to exp(S - m) with the final maximum.
+    Key tiles of `tile` keys in order; per query row, with m = -inf, l = 0,
+    O = 0:
+        S_j = s Q K_j^T (causal mask -inf), m' = max(m, rowmax S_j),
+        a = exp(m - m'),  P~_j = exp(S_j - m'),
+        O = a O + fp8(P~_j) V_j,  l = a l + rowsum P~_j,  m = m'
+    then O / l and L = m + ln l. `quant` replaces fp8 (identity: plain
+    attention). q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]; float64 results."""
+    quant = quantize_probs if quant is None else quant
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, Hq, Nq, _ = q.shape
+    G = Hq // k.shape[1]
+    Nk = k.shape[2]
+    O = np.empty((B, Hq, Nq, v.shape[-1]))
+    L = np.empty((B, Hq, Nq))
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            m = np.full(Nq, -np.inf)
+            ell = np.zeros(Nq)
+            acc = np.zeros((Nq, v.shape[-1]))
+            for j0 in range(0, Nk, tile):
+                cols = np.arange(j0, min(Nk, j0 + tile))
+                S = float(scale) * (q[b, h] @ k[b, g, cols].T)
+                if causal:
+                    S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+                m_new = np.maximum(m, S.max(axis=1))
+                seen = m_new > -np.inf  # rows with no visible key yet keep O = 0, l = 0
+                alpha = np.where(seen, np.exp(np.where(seen, m - m_new, 0.0)), 1.0)
+                Pt = np.where(seen[:, None], np.exp(S - np.where(seen, m_new, 0.0)[:, None]), 0.0)
+                acc = alpha[:, None] * acc + quant(Pt) @ v[b, g, cols]
+                ell = alpha * ell + Pt.sum(axis=1)
+                m = m_new
+            O[b, h] = acc / ell[:, None]
+            L[b, h] = m + np.log(ell)
+    return O, L
+
+
 def forward_fp8(q, k, v, scale, causal, signs=None, per_tensor=False, v_fp8=False, p_fp8=False):
     """The FP8 forward: quantize Q and K (same signs; 64-row block scales, or
     one scale per tensor), optionally V (never transformed) and P, then the

@@ -277,3 +277,31 @@ def test_page_outlier_experiment_per_tensor_against_incoherent_block_fp8():
         ratios.append(np.sqrt(np.mean((std - O) ** 2)) / np.sqrt(np.mean((inc - O) ** 2)))
     print(f"rmse(standard FP8) / rmse(incoherent, block scales): {ratios}")
     assert min(ratios) > 1.4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_probs_fp8_reduces_to_the_direct_definitions(causal):
+    rng = np.random.default_rng(45 + causal)
+    q = rng.standard_normal((1, 2, 150, 16)) * 1.5
+    k = rng.standard_normal((1, 1, 150, 16))
+    v = rng.standard_normal((1, 1, 150, 16))
+    # one tile over all keys: the running maximum is the final one
+    O1, L1 = fp8.forward_probs_fp8_online(q, k, v, 0.3, causal, tile=150)
+    O2, L2 = fp8.forward_probs_fp8(q, k, v, 0.3, causal)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
+    # without the rounding, any tiling gives exact attention (the online
+    # softmax identity)
+    O0, L0 = oracle.forward(q, k, v, 0.3, causal)
+    for tile in (1, 7, 64):
+        O3, L3 = fp8.forward_probs_fp8_online(q, k, v, 0.3, causal, tile=tile, quant=lambda p: p)
+        np.testing.assert_allclose(O3, O0, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L3, L0, rtol=0, atol=1e-12)
+    # with it, a tiling differs from the direct rounding by at most one e4m3
+    # step (2^-3 relative) per probability, and L never sees the rounding
+    O4, L4 = fp8.forward_probs_fp8_online(q, k, v, 0.3, causal, tile=64)
+    np.testing.assert_allclose(L4, L0, rtol=0, atol=1e-12)
+    assert np.max(np.abs(O4 - O2)) <= 2.0 ** -3 * np.max(np.abs(v)) + 1e-12
+    if causal:
+        for h in range(2):
+            np.testing.assert_array_equal(O4[0, h, 0], v[0, 0, 0])  # row 0: one key, P~ = 1 exactly
