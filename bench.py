@@ -543,9 +543,11 @@ MI355X_FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA
 def bench_fp8(args):
     """Time the FP8 forward path on one forward workload: fa_quantize_fp8 of
     Q and of K (random-sign Hadamard transform, seed = the workload's) and
-    fa_fwd_fp8 (bf16 O), with fa_fwd on the same inputs beside it. Prints one
+    fa_fwd_fp8 (bf16 O), with fa_fwd on the same inputs beside it, then
+    fa_quantize_vt_fp8 of V and fa_fwd_fp8_pv (P V in FP8 too). Prints one
     JSON line. The roofline of fa_fwd_fp8 counts S = Q K^T at the fp8 peak
-    and O = P V at the bf16 peak: half of the flops each."""
+    and O = P V at the bf16 peak (half of the flops each); that of
+    fa_fwd_fp8_pv counts both at the fp8 peak."""
     import torch
     from exact_tiled_attention_28_amd.inputs import make_signs
     from exact_tiled_attention_28_amd.workloads import Workload
@@ -573,8 +575,17 @@ def bench_fp8(args):
     def fwd8():
         binding.forward_fp8(qc, qs, kc, ks, v, w.scale, w.causal, o=o, lse=lse, stream=stream)
 
-    _, per_call, _ = time_calls(None, [quant_q, quant_k, fwd8, step.fwd], args.steps, args.warmup)
-    med = [float(np.median(per_call[:, i])) for i in range(4)]
+    vt, vs = binding.quantize_vt_fp8(v)
+
+    def quant_v():
+        binding.quantize_vt_fp8(v, vt, vs, stream=stream)
+
+    def fwd8pv():
+        binding.forward_fp8_pv(qc, qs, kc, ks, vt, vs, w.scale, w.causal, o=o, lse=lse, stream=stream)
+
+    _, per_call, _ = time_calls(None, [quant_q, quant_k, fwd8, step.fwd, quant_v, fwd8pv], args.steps, args.warmup)
+    med = [float(np.median(per_call[:, i])) for i in range(6)]
+    avgpv = float(np.mean(per_call[:, 5]))
     avg8 = float(np.mean(per_call[:, 2]))
     ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
     peak_mixed = 2.0 / (1.0 / MI355X_FP8_PEAK_TFLOPS + 1.0 / MI355X_BF16_PEAK_TFLOPS)
@@ -589,6 +600,14 @@ def bench_fp8(args):
            "fp8_path_ms": round(sum(med[:3]), 4),
            "fp8_path_tflops": round(ff / (sum(med[:3]) * 1e-3) / 1e12, 2),
            "fwd_bf16_ms": round(med[3], 4), "fwd_bf16_tflops": round(ff / (med[3] * 1e-3) / 1e12, 2),
+           "quantize_vt_ms": round(med[4], 4),
+           "fwd_fp8_pv_ms": round(med[5], 4), "fwd_fp8_pv_tflops": round(ff / (med[5] * 1e-3) / 1e12, 2),
+           "fp8_pv_path_ms": round(med[0] + med[1] + med[4] + med[5], 4),
+           "roofline_fp8_pv": {"kernel": "fa_fwd_fp8_pv (fwd_fp8_kernel, P V in FP8)", "bound": "mfma",
+                               "achieved": round(ff / (avgpv * 1e-3) / 1e12, 2), "peak": MI355X_FP8_PEAK_TFLOPS,
+                               "unit": "TFLOP/s",
+                               "frac": round(ff / (avgpv * 1e-3) / 1e12 / MI355X_FP8_PEAK_TFLOPS, 4),
+                               "avg_launch_ms": round(avgpv, 4)},
            "roofline": {"kernel": "fa_fwd_fp8 (fwd_fp8_kernel)", "bound": "mfma", "achieved": round(ach, 2),
                         "peak": round(peak_mixed, 1), "unit": "TFLOP/s", "frac": round(ach / peak_mixed, 4),
                         "peak_note": "half the flops (Q K^T) at the 5.0 PFLOP/s fp8 peak, half (P V) at the "

@@ -84,6 +84,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.fa_fp8_scales_count.argtypes = [_c_int] * 3
         lib.fa_fwd_fp8.restype = _c_int
         lib.fa_fwd_fp8.argtypes = [_c_ptr] * 7 + [_c_int] * 6 + [_c_float] + [_c_int] * 2 + [_c_ptr]
+    if hasattr(lib, "fa_quantize_vt_fp8"):
+        lib.fa_quantize_vt_fp8.restype = _c_int
+        lib.fa_quantize_vt_fp8.argtypes = [_c_ptr] * 3 + [_c_int] * 5 + [_c_ptr]
+        lib.fa_fp8_vt_bytes.restype = ctypes.c_size_t
+        lib.fa_fp8_vt_bytes.argtypes = [_c_int] * 4
+        lib.fa_fwd_fp8_pv.restype = _c_int
+        lib.fa_fwd_fp8_pv.argtypes = [_c_ptr] * 8 + [_c_int] * 6 + [_c_float] + [_c_int] * 2 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -165,6 +172,22 @@ def fa_fwd_fp8(q_codes, q_scales, k_codes, k_scales, v, o, lse, batch, n_q_heads
                head_dim, scale, causal, out_dtype, stream) -> int:
     return load_library().fa_fwd_fp8(q_codes, q_scales, k_codes, k_scales, v, o, lse, batch, n_q_heads, n_kv_heads,
                                      seqlen_q, seqlen_k, head_dim, scale, causal, out_dtype, stream)
+
+
+def fa_quantize_vt_fp8(v, vt_codes, block_scales, batch, n_heads, seqlen, head_dim, in_dtype, stream) -> int:
+    return load_library().fa_quantize_vt_fp8(v, vt_codes, block_scales, batch, n_heads, seqlen, head_dim, in_dtype,
+                                             stream)
+
+
+def fa_fp8_vt_bytes(batch, n_heads, seqlen, head_dim) -> int:
+    return load_library().fa_fp8_vt_bytes(batch, n_heads, seqlen, head_dim)
+
+
+def fa_fwd_fp8_pv(q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, o, lse, batch, n_q_heads, n_kv_heads,
+                  seqlen_q, seqlen_k, head_dim, scale, causal, out_dtype, stream) -> int:
+    return load_library().fa_fwd_fp8_pv(q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, o, lse, batch,
+                                        n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim, scale, causal, out_dtype,
+                                        stream)
 
 
 def fa_bwd_workspace_bytes(batch, n_q_heads, seqlen_q) -> int:
@@ -379,4 +402,53 @@ def forward_persistent(q, k, v, scale, causal, sched, out_dtype=None, o=None, ls
                            B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q), oc,
                            _stream_handle(stream))
     _check(rc, "fa_fwd_persistent")
+    return o, lse
+
+
+def quantize_vt_fp8(v, codes=None, scales=None, stream=None):
+    """Transposed FP8 codes of V for forward_fp8_pv (uint8
+    [B,H,ceil(N/64),d,64], see fa_quantize_vt_fp8 for the key order within a
+    block) and the power-of-two block scales (fp32 [B,H,ceil(N/64)]) of
+    v [B,H,N,d] (contiguous bf16 on the GPU)."""
+    import torch
+    B, H, N, d = v.shape
+    nb = -(-N // 64)
+    if codes is None:
+        codes = torch.empty((B, H, nb, d, 64), dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=v.device)
+    for t in (v, codes, scales):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if codes.numel() != fa_fp8_vt_bytes(B, H, N, d):
+        raise ValueError("codes must hold fa_fp8_vt_bytes(B, H, N, d) bytes")
+    rc = fa_quantize_vt_fp8(v.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d, _dtype_code(v),
+                            _stream_handle(stream))
+    _check(rc, "fa_quantize_vt_fp8")
+    return codes, scales
+
+
+def forward_fp8_pv(q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, scale, causal, out_dtype=None, o=None,
+                   lse=None, stream=None):
+    """O, L of the FP8 forward with P V in FP8 as well: Q, K codes and scales
+    from quantize_fp8, V from quantize_vt_fp8."""
+    import torch
+    B, Hq, Nq, d = q_codes.shape
+    Hkv, Nk = k_codes.shape[1], k_codes.shape[2]
+    oc = FA_DTYPE_BF16 if out_dtype in (None, torch.bfloat16) else FA_DTYPE_F32
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=_torch_dtype(oc), device=q_codes.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q_codes.device)
+    for t in (q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if vt_codes.numel() != fa_fp8_vt_bytes(B, Hkv, Nk, d):
+        raise ValueError("vt_codes must hold fa_fp8_vt_bytes(B, Hkv, Nk, d) bytes")
+    rc = fa_fwd_fp8_pv(q_codes.data_ptr(), q_scales.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(),
+                       vt_codes.data_ptr(), v_scales.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                       float(scale), int(bool(causal)), oc, _stream_handle(stream))
+    _check(rc, "fa_fwd_fp8_pv")
     return o, lse

@@ -332,6 +332,71 @@ int fa_fwd_fp8(const void* q_codes, const float* q_scales, const void* k_codes, 
   return hip_status(e, "fa_fwd_fp8 launch");
 }
 
+int fa_quantize_vt_fp8(const void* v, void* vt_codes, float* block_scales, int batch, int n_heads, int seqlen,
+                       int head_dim, int in_dtype, void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_ptr(v, "v", err)) || (rc = fa::check_ptr(vt_codes, "vt_codes", err))) return fail(rc, err);
+  if (block_scales == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "block_scales is NULL");
+  if (reinterpret_cast<uintptr_t>(block_scales) & 3u)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_scales is not 4-byte aligned");
+  if (batch < 1 || n_heads < 1 || seqlen < 1) return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1");
+  if (!fa::valid_dtype(in_dtype)) return fail(FA_ERR_INVALID_ARGUMENT, "in_dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16");
+  if (in_dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "fa_quantize_vt_fp8 takes bf16 input");
+  if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim " + std::to_string(head_dim) +
+                                                     " unsupported (64 or 128)");
+  if ((long long)seqlen * head_dim >= (1LL << 31)) return fail(FA_ERR_INVALID_ARGUMENT, "seqlen * head_dim must be below 2^31");
+  if ((long long)batch * n_heads * (((long long)seqlen + 63) / 64) >= (1LL << 31))
+    return fail(FA_ERR_INVALID_ARGUMENT, "batch * n_heads * blocks too large");
+  hipError_t e = fa::launch_quantize_vt_fp8(v, vt_codes, block_scales, batch * n_heads, seqlen, head_dim,
+                                            (hipStream_t)stream);
+  return hip_status(e, "fa_quantize_vt_fp8 launch");
+}
+
+size_t fa_fp8_vt_bytes(int batch, int n_heads, int seqlen, int head_dim) {
+  if (batch <= 0 || n_heads <= 0 || seqlen <= 0 || head_dim <= 0) return 0;
+  return (size_t)batch * (size_t)n_heads * (((size_t)seqlen + 63) / 64) * 64 * (size_t)head_dim;
+}
+
+int fa_fwd_fp8_pv(const void* q_codes, const float* q_scales, const void* k_codes, const float* k_scales,
+                  const void* vt_codes, const float* v_scales, void* o, float* lse, int batch, int n_q_heads,
+                  int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal, int out_dtype,
+                  void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_fwd(q_codes, k_codes, vt_codes, o, lse,
+                          fa::Shape{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim}, scale, causal,
+                          FA_DTYPE_BF16, out_dtype, err)))
+    return fail(rc, err);
+  if (q_scales == nullptr || k_scales == nullptr || v_scales == nullptr)
+    return fail(FA_ERR_INVALID_ARGUMENT, q_scales == nullptr ? "q_scales is NULL"
+                                         : (k_scales == nullptr ? "k_scales is NULL" : "v_scales is NULL"));
+  if ((reinterpret_cast<uintptr_t>(q_scales) & 3u) || (reinterpret_cast<uintptr_t>(k_scales) & 3u) ||
+      (reinterpret_cast<uintptr_t>(v_scales) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "q_scales / k_scales / v_scales must be 4-byte aligned");
+  if ((long long)batch * n_kv_heads * (((long long)seqlen_k + 63) / 64) * 64 * head_dim >= (1LL << 40))
+    return fail(FA_ERR_INVALID_ARGUMENT, "vt_codes too large");
+  fa::FwdArgs a{};
+  a.q = q_codes;
+  a.k = k_codes;
+  a.v = vt_codes;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  a.q_scales = q_scales;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  hipError_t e = fa::launch_fwd_fp8(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  return hip_status(e, "fa_fwd_fp8_pv launch");
+}
+
 size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen) {
   if (batch <= 0 || n_heads <= 0 || seqlen <= 0) return 0;
   return (size_t)batch * (size_t)n_heads * (((size_t)seqlen + 63) / 64);

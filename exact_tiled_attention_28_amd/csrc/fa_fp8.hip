@@ -175,6 +175,95 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const 
 }
 
 // ---------------------------------------------------------------------------
+// V for the FP8 P V product: fa_quantize_vt_fp8 writes V transposed, one
+// 64-key block at a time, as e4m3 codes of V / 2^e with the block's
+// power-of-two scale 2^e (the same rule as above, no transform: only Q and K
+// may be rotated). Layout [head][block][d][64]: row c of a block holds
+// channel c of its 64 keys, in the order in which a lane of half-wave g of
+// the FP8 product holds its probabilities: position 32 g + s, s < 32, holds
+// key 32 (s / 16) + 8 ((s % 16) / 4) + 4 g + s % 4 of the block (the order of
+// the S^T accumulator registers), so that the forward reads its A operand
+// with plain 16-byte loads and feeds P from registers. Keys past the end get
+// code 0. This is the transpose that the FP8 product needs, done once in the
+// quantize pass that reads and rewrites V anyway.
+// One workgroup per 64-key block of one head: the block goes through LDS
+// (bf16, row-major), the block maximum by shuffles and 4 LDS words, and each
+// thread writes whole 16-byte chunks of the transposed rows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vt_key_of(int pos) {
+  const int g = pos >> 5, s = pos & 31;
+  return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * g + (s & 3);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) quantize_vt_fp8_kernel(const __bf16* __restrict__ x,
+                                                               uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales, int N, int n_blocks) {
+  constexpr int RCH = D / 8;              // 16-byte chunks per bf16 row
+  constexpr int LPT = 64 * RCH / 256;     // chunks loaded per thread
+  constexpr int SPT = D * 4 / 256;        // 16-byte output chunks per thread
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * D];
+  __shared__ float wmax[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int head = blockIdx.x / n_blocks, blk = blockIdx.x % n_blocks;
+  const int k0 = blk * 64;
+  const __bf16* xh = x + (size_t)head * N * D;
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int ci = tid + 256 * u;
+    const int row = ci / RCH, cc = ci % RCH;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (k0 + row < N) raw = *(const u32x4*)(xh + (size_t)(k0 + row) * D + 8 * cc);
+    *(u32x4*)(tile + row * D + 8 * cc) = raw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[i] << 16)), fabsf(__uint_as_float(raw[i] & 0xFFFF0000u))));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (lane == 0) wmax[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int e2 = block_scale_exp(amax);
+  if (tid == 0) scales[blockIdx.x] = ldexpf(1.0f, e2);
+
+  uint8_t* out = codes + (size_t)blockIdx.x * D * 64;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int oi = tid + 256 * u;
+    const int c = oi >> 2, p0 = 16 * (oi & 3);  // channel c, positions p0 .. p0 + 15
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      unsigned word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = (float)tile[vt_key_of(p0 + 4 * i + j) * D + c];
+        word |= e4m3_code(ldexpf(v, -e2)) << (8 * j);
+      }
+      o[i] = word;
+    }
+    *(u32x4*)(out + c * 64 + p0) = o;
+  }
+}
+
+hipError_t launch_quantize_vt_fp8(const void* v, void* codes, float* scales, int heads, int N, int head_dim,
+                                  hipStream_t s) {
+  const int n_blocks = ceil_div(N, 64);
+  const long long grid = (long long)heads * n_blocks;
+  if (head_dim == 64)
+    hipLaunchKernelGGL((quantize_vt_fp8_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, (const __bf16*)v,
+                       (uint8_t*)codes, scales, N, n_blocks);
+  else
+    hipLaunchKernelGGL((quantize_vt_fp8_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, (const __bf16*)v,
+                       (uint8_t*)codes, scales, N, n_blocks);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // FP8 forward, d = 64 and 128: fwd_kernel's tiling (4 wavefronts x 32 query
 // rows, 64-key tiles, K/V in LDS filled by HBM -> LDS loads) with the K tile
 // held as e4m3 codes (d bytes per row: 8 KiB at d = 128, 4 KiB at 64) and
@@ -187,12 +276,22 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const 
 // scores of a tile are scaled by one scalar s_q s_k, folded into the base-2
 // softmax constant.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool OUTF32>
+// PV8: P V in FP8 as well (fa_fwd_fp8_pv): V arrives as the transposed codes
+// of fa_quantize_vt_fp8 (tile j = 64 keys x D channels, contiguous, row c =
+// channel c), P is packed to e4m3 at the fixed scale 2^8 straight from the
+// S^T accumulator registers (whose order the V^T rows follow), and
+// O^T += V^T P^T is one 32x32x64 FP8 product per 32 channels. The running
+// sum l stays in fp32 over the unrounded probabilities; the V block scale of
+// each tile is applied by keeping the accumulator in units of the current
+// tile's scale (a power-of-two rescale, skipped while the scale repeats).
+template <int D, bool CAUSAL, bool OUTF32, bool PV8 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_fp8_kernel(FwdArgs a) {
   constexpr int NW = 4, BR = 128, BC = 64, NKB = 2, NKS = D / 64, NDB = D / 32;
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
   constexpr int KROWB = D, KRC = KROWB / 16, KTILEB = BC * KROWB, KCPW = KTILEB / (1024 * NW);  // fp8 K tile
-  constexpr int VROWB = D * 2, VRC = VROWB / 16, VTILEB = BC * VROWB, VCPW = VTILEB / (1024 * NW);  // bf16 V
+  // V tile: bf16 rows of D channels, or (PV8) D rows of 64 key codes
+  constexpr int VROWB = PV8 ? BC : D * 2, VRC = VROWB / 16, VTILEB = PV8 ? D * BC : BC * VROWB;
+  constexpr int VCPW = VTILEB / (1024 * NW);
   static_assert(KTILEB % (1024 * NW) == 0 && VTILEB % (1024 * NW) == 0, "tiles must split into whole wave loads");
 
   // Three K buffers and two V buffers (56 KiB at d = 128): K_j is fetched two steps
@@ -225,7 +324,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const size_t qhead = (size_t)(b * a.Hq + hq) * Nq;
   const size_t kvhead = (size_t)(b * a.Hkv + hkv) * Nk;
   const char* __restrict__ Kh = uniform_ptr((const char*)a.k + kvhead * KROWB);
-  const char* __restrict__ Vh = uniform_ptr((const char*)a.v + kvhead * VROWB);
+  // (PV8: the transposed code tiles of this K/V head, ceil(Nk / 64) tiles of
+  // D * 64 bytes)
+  const char* __restrict__ Vh =
+      uniform_ptr((const char*)a.v + (PV8 ? (size_t)(b * a.Hkv + hkv) * ceil_div(Nk, 64) * (D * 64) : kvhead * VROWB));
   const int nqb = ceil_div(Nq, 64), nkb = ceil_div(Nk, 64);
   // A wavefront whose rows all lie past the end (last query tile) stores
   // nothing; its block index is clamped to stay inside the scale array.
@@ -277,12 +379,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr int CPWX = decltype(ncpw)::value;
     const int kv0 = jt * BC;
-    const char* Xb = uniform_ptr(Xh + (size_t)kv0 * rowb);
+    const char* Xb = uniform_ptr(Xh + (size_t)kv0 * (rowb != 0 ? rowb : D));
     const unsigned last = (unsigned)(Nk - 1 - kv0);  // last row of K/V in this tile
 #pragma unroll
     for (int u = 0; u < CPWX; ++u) {
       unsigned ou = (unsigned)ld[u];
-      if (!FULL && kv0 + BC > Nk && ou / rowb > last) ou = last * rowb + ou % rowb;
+      if (!FULL && rowb != 0 && kv0 + BC > Nk && ou / rowb > last) ou = last * rowb + ou % rowb;
       asm volatile("" : "+v"(ou));
       load_lds_16(Xb + ou, Xt + (wu * CPWX + u) * 64 * 16);
     }
@@ -290,8 +392,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto issue_k = [&](auto full_tag, int jt, char* Kt) __attribute__((always_inline)) {
     issue(full_tag, jt, Kh, kld, std::integral_constant<int, KCPW>{}, KROWB, Kt);
   };
+  // (rowb 0: a transposed code tile, D bytes per key, never clamped)
   auto issue_v = [&](auto full_tag, int jt, char* Vt) __attribute__((always_inline)) {
-    issue(full_tag, jt, Vh, vld, std::integral_constant<int, VCPW>{}, VROWB, Vt);
+    issue(full_tag, jt, Vh, vld, std::integral_constant<int, VCPW>{}, PV8 ? 0 : VROWB, Vt);
   };
 
   int koff[NKS][2];
@@ -300,7 +403,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int h = 0; h < 2; ++h) koff[ks][h] = tile_off<KRC>(l32, (4 * ks + 2 * g + h) * 16);
   int voff[NDB][2];
-  {
+  if constexpr (PV8) {
+    // A operand of the FP8 P V product: channel row 32 db + l32, the 32 codes
+    // of half-wave g (two 16-byte reads); the swizzle of a 64-byte row depends
+    // on the row mod 16 only, so channel blocks add constants
+#pragma unroll
+    for (int h = 0; h < 2; ++h) voff[0][h] = tile_off<VRC>(l32, (2 * g + h) * 16);
+  } else {
     const int j = lane & 15;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -308,6 +417,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int h = 0; h < 2; ++h)
         voff[db][h] = tile_off<VRC>(4 * g + 8 * h + (j >> 2), (db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)) * 2);
   }
+  // PV8: the V block scale the accumulator is currently expressed in
+  const float* __restrict__ svp = PV8 ? a.v_scales + (size_t)(b * a.Hkv + hkv) * nkb : nullptr;
+  float sv_ref = PV8 ? svp[0] : 1.0f;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -321,7 +433,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // c: |scale| log2(e) times the Q block scale and this tile's K block scale,
   // raised to at least the smallest normal float (a zero scale then gives
   // every visible key probability exactly 1 before normalisation)
-  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt, float c) __attribute__((always_inline)) {
+  auto body = [&](auto mask_tag, int jt, const char* Kt, const char* Vt, float c, float sv) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = jt * BC;
     f32x16 sacc[NKB];
@@ -362,15 +474,43 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
     float rs = 0.0f;
+    // PV8: P 2^8 (the FP8 codes' scale; l is kept scaled alike, exact)
+    const float moff = PV8 ? 8.0f - m : -m;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
+        const float p = fast_exp2(fmaf(sacc[kb][r], c, moff));
         sacc[kb][r] = p;
         rs += p;
       }
     lsum += rs;
+    if constexpr (PV8) {
+      // slot s = 16 kb + r of this half-wave: register r of block kb
+      i32x8 pc;
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) {
+        const int kb = wd >> 2, r0 = 4 * (wd & 3);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][r0], sacc[kb][r0 + 1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][r0 + 2], sacc[kb][r0 + 3], x, true);
+        pc[wd] = x;
+      }
+      if (sv != sv_ref) {  // uniform: a power-of-two change of units, exact
+        const float f = sv_ref / sv;
+        sv_ref = sv;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= f;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vb = Vt + db * 32 * VROWB;
+        const u32x4 a0 = *(const u32x4*)(vb + voff[0][0]);
+        const u32x4 a1 = *(const u32x4*)(vb + voff[0][1]);
+        const i32x8 va = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pc, oacc[db], 0, 0, 0, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < BC / 16; ++t) {
       float pv[8];
@@ -399,6 +539,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NTAIL = BR / BC;
   const int n_fast = max(0, min(min(n_kv - NTAIL, n_kv - 2), Nk / BC - 2));
   float c_next = 0.0f, c_cur = 0.0f;  // K block scale of the next tile; this tile's score factor
+  float sv_next = 1.0f, sv_cur = sv_ref;  // PV8: V block scale of the next tile, of this tile
   auto step = [&](auto generic_tag, int jt, const char* Kt, const char* Vt, char* Vn, char* Kn2)
                   __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
@@ -407,20 +548,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     // The next tile's K block scale is loaded before this step's tile loads,
     // so the end-of-step wait covers it and nothing waits on it earlier.
     const float c = c_cur;
+    const float sv = sv_cur;
     if (has1) c_next = sk[jt + 1];
+    if constexpr (PV8)
+      if (has1) sv_next = svp[jt + 1];
     if (has1) issue_v(std::bool_constant<!GENERIC>{}, jt + 1, Vn);
     if (has2) issue_k(std::bool_constant<!GENERIC>{}, jt + 2, Kn2);
     if constexpr (GENERIC) {
-      if (!CAUSAL || jt * BC <= q0w + 31) body(std::true_type{}, jt, Kt, Vt, c);
+      if (!CAUSAL || jt * BC <= q0w + 31) body(std::true_type{}, jt, Kt, Vt, c, sv);
       if (has2)
         wait_vmem_n<KCPW>();
       else
         wait_vmem_n<0>();
     } else {
-      body(std::false_type{}, jt, Kt, Vt, c);
+      body(std::false_type{}, jt, Kt, Vt, c, sv);
       wait_vmem_n<KCPW>();
     }
     c_cur = fmaxf(a.c * sq * c_next, FLT_MIN);
+    sv_cur = sv_next;
     wait_lds();
     lds_barrier();
   };
@@ -467,7 +612,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   const float lt = half_swap_add(lsum);
-  const float inv = 1.0f / lt;
+  // PV8: O = acc 2^e_v / (2^8 l), with lt = 2^8 l
+  const float inv = (PV8 ? sv_ref : 1.0f) / lt;
   if (qrow < Nq) {
     const size_t orow = (qhead + qrow) * D;
 #pragma unroll
@@ -482,22 +628,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         else
           *(bf16x4*)((__bf16*)a.o + orow + d0) = __builtin_convertvector(ov, bf16x4);
       }
-    if (g == 0) a.lse[qhead + qrow] = (m + fast_log2(lt)) * kLn2;
+    if (g == 0) a.lse[qhead + qrow] = (m + fast_log2(lt) - (PV8 ? 8.0f : 0.0f)) * kLn2;
   }
 }
 
-template <int D>
+template <int D, bool PV8>
 static void launch_fwd_fp8_d(const FwdArgs& a, long long blocks, bool causal, bool out_f32, hipStream_t s) {
   if (causal) {
     if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {
     if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   }
 }
 
@@ -505,10 +651,18 @@ hipError_t launch_fwd_fp8(const FwdArgs& a0, int head_dim, bool causal, bool out
   FwdArgs a = a0;
   a.n_q_tiles = ceil_div(a.Nq, 128);
   const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
-  if (head_dim == 64)
-    launch_fwd_fp8_d<64>(a, blocks, causal, out_f32, s);
-  else
-    launch_fwd_fp8_d<128>(a, blocks, causal, out_f32, s);
+  const bool pv8 = a.v_scales != nullptr;
+  if (head_dim == 64) {
+    if (pv8)
+      launch_fwd_fp8_d<64, true>(a, blocks, causal, out_f32, s);
+    else
+      launch_fwd_fp8_d<64, false>(a, blocks, causal, out_f32, s);
+  } else {
+    if (pv8)
+      launch_fwd_fp8_d<128, true>(a, blocks, causal, out_f32, s);
+    else
+      launch_fwd_fp8_d<128, false>(a, blocks, causal, out_f32, s);
+  }
   return hipGetLastError();
 }
 

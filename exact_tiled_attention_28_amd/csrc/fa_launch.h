@@ -26,6 +26,10 @@ struct FwdArgs {
   // of each 64-row block, [B][Hq][ceil(Nq/64)] and [B][Hkv][ceil(Nk/64)].
   const float* q_scales;
   const float* k_scales;
+  // FP8 P V (fa_fwd_fp8_pv): v holds the transposed codes of
+  // fa_quantize_vt_fp8 and v_scales their block scales [B][Hkv][ceil(Nk/64)];
+  // null for the bf16 V of fa_fwd_fp8.
+  const float* v_scales;
   // Persistent forward (fa_fwd_persistent): 9 work-queue counters, zero on
   // entry and left zero on exit.
   int* sched;
@@ -62,6 +66,8 @@ hipError_t launch_fwd_persistent(const FwdArgs& a, int head_dim, bool causal, bo
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, const signed char* signs, int heads,
                                int N, int head_dim, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, bool causal, bool out_f32, hipStream_t s);
+hipError_t launch_quantize_vt_fp8(const void* v, void* codes, float* scales, int heads, int N, int head_dim,
+                                  hipStream_t s);
 // fa_bwd_noalloc keeps D in a static device array of this many fp32 rows
 // (16 MiB per device); bwd_noalloc_scratch returns its device address on the
 // current device (looked up once per device, with hipGetSymbolAddress).

@@ -273,6 +273,48 @@ int fa_quantize_fp8(const void* x, void* codes, float* block_scales,
 size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen);
 
 /*
+ * fa_quantize_vt_fp8 — V for the FP8 P V product (fa_fwd_fp8_pv): per 64-key
+ * block of one head, the power-of-two scale 2^e with max|v| <= 448 * 2^e
+ * (as fa_quantize_fp8, no transform) and the e4m3 codes of v / 2^e (round to
+ * nearest even), written transposed: block j of head h occupies
+ * vt_codes[((h * ceil(N/64)) + j) * d * 64 ..] as d rows of 64 codes, row c
+ * holding channel c of the block's keys in the order the forward's product
+ * consumes them: position 32 g + s (g = 0, 1; s < 32) holds key
+ * 32 (s / 16) + 8 ((s % 16) / 4) + 4 g + s % 4 of the block; keys past N get
+ * code 0. (FlashAttention-3 news page, "Độ chính xác thấp FP8 và incoherent
+ * processing", and its mention of the FP8 transpose: the transpose is done
+ * here, in the pass that rewrites V anyway.)
+ *   v            device, bf16 [B][H][N][d], 16-byte aligned
+ *   vt_codes     device, uint8, fa_fp8_vt_bytes(B, H, N, d) bytes, 16-byte aligned
+ *   block_scales device, fp32 [B][H][ceil(N/64)], 4-byte aligned
+ * head_dim 64 or 128; in_dtype FA_DTYPE_BF16. Asynchronous on stream.
+ */
+int fa_quantize_vt_fp8(const void* v, void* vt_codes, float* block_scales,
+                       int batch, int n_heads, int seqlen, int head_dim,
+                       int in_dtype, void* stream);
+
+/* Bytes fa_quantize_vt_fp8 writes: batch * n_heads * ceil(seqlen / 64) * 64
+ * * head_dim (0 for non-positive arguments). */
+size_t fa_fp8_vt_bytes(int batch, int n_heads, int seqlen, int head_dim);
+
+/*
+ * fa_fwd_fp8_pv — fa_fwd_fp8 with the second product in FP8 as well: P is
+ * rounded to e4m3 at the fixed scale 2^8 against the running row maximum of
+ * the key tiles seen so far (the largest probability is exactly 1), V comes
+ * as the transposed codes and block scales of fa_quantize_vt_fp8, and
+ * O^T += V^T P^T runs on the FP8 matrix cores; the row sum l is accumulated
+ * in fp32 over the unrounded probabilities, so L is that of fa_fwd_fp8.
+ *   q_codes, q_scales, k_codes, k_scales as in fa_fwd_fp8 (d = 64 or 128);
+ *   vt_codes, v_scales as written by fa_quantize_vt_fp8 for V [B][Hkv][Nk][d];
+ *   o, lse, scale, causal, out_dtype as in fa_fwd.
+ */
+int fa_fwd_fp8_pv(const void* q_codes, const float* q_scales, const void* k_codes,
+                  const float* k_scales, const void* vt_codes, const float* v_scales,
+                  void* o, float* lse, int batch, int n_q_heads, int n_kv_heads,
+                  int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                  int out_dtype, void* stream);
+
+/*
  * fa_fwd_fp8 — fa_fwd with the scores formed in FP8: q_codes / k_codes and
  * q_scales / k_scales as written by fa_quantize_fp8 (with the same signs for
  * Q and K), S = scale * (Q_codes 2^e_q)(K_codes 2^e_k)^T by FP8 matrix cores

@@ -132,6 +132,14 @@ int main() {
                     FA_DTYPE_BF16, nullptr) == FA_OK);
   EXPECT(fa_fwd_fp8(P, (const float*)P, P, (const float*)P, P, P, (float*)P, 1, 2, 1, 64, 64, 96, 0.1f, 0,
                     FA_DTYPE_BF16, nullptr) == FA_ERR_UNSUPPORTED);
+  EXPECT(fa_quantize_vt_fp8(P, P, (float*)P, 2, 4, 1000, 64, FA_DTYPE_BF16, nullptr) == FA_OK);
+  EXPECT(fa_quantize_vt_fp8(P, P, (float*)P, 2, 4, INT_MAX, 128, FA_DTYPE_BF16, nullptr) ==
+         FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fp8_vt_bytes(INT_MAX, INT_MAX, INT_MAX, 128) > 0);
+  EXPECT(fa_fwd_fp8_pv(P, (const float*)P, P, (const float*)P, P, (const float*)P, P, (float*)P, 1, 2, 1, 64, 64,
+                       128, 0.1f, 1, FA_DTYPE_F32, nullptr) == FA_OK);
+  EXPECT(fa_fwd_fp8_pv(P, (const float*)P, P, (const float*)P, P, nullptr, P, (float*)P, 1, 2, 1, 64, 64, 128, 0.1f,
+                       1, FA_DTYPE_F32, nullptr) == FA_ERR_INVALID_ARGUMENT);
   EXPECT(fa_fwd_persistent(P, P, P, P, (float*)P, (int*)P, 1, 2, 1, 64, 64, 128, 0.1f, 1, FA_DTYPE_BF16,
                            FA_DTYPE_BF16, nullptr) == FA_OK);
   EXPECT(fa_fwd_persistent(P, P, P, P, (float*)P, (int*)(uintptr_t{0x10002}), 1, 2, 1, 64, 64, 128, 0.1f, 1,

@@ -45,6 +45,10 @@ hipError_t launch_quantize_fp8(const void*, void*, float*, const signed char*, i
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_quantize_vt_fp8(const void*, void*, float*, int, int, int, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_fwd_fp8(const FwdArgs& a, int, bool, bool, hipStream_t) {
   g_last_fwd = a;
   ++g_launches;

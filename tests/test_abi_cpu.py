@@ -35,9 +35,9 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
-        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count", "fa_fwd",
-         "fa_fwd_fp8", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes", "fa_fwd_varlen", "fa_last_error",
-         "fa_quantize_fp8", "fa_status_string", "fa_version"])
+        ["fa_bwd", "fa_bwd_atomic", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count",
+         "fa_fp8_vt_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_pv", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes",
+         "fa_fwd_varlen", "fa_last_error", "fa_quantize_fp8", "fa_quantize_vt_fp8", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_function(lib):
@@ -306,6 +306,57 @@ def test_quantize_fp8_argument_errors(lib, kw, code, text):
 def test_fwd_fp8_argument_errors(lib, kw, code, text):
     assert fwd_fp8(**kw) == code
     assert text in binding.fa_last_error()
+
+
+def quantize_vt_fp8(**kw):
+    args = dict(v=P, codes=P, scales=CU, batch=1, n_heads=2, seqlen=100, head_dim=128, in_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_quantize_vt_fp8(*args.values())
+
+
+def fwd_fp8_pv(**kw):
+    args = dict(q=P, qs=CU, k=P, ks=CU, vt=P, vs=CU, o=P, lse=P, batch=1, n_q_heads=2, n_kv_heads=1, seqlen_q=16,
+                seqlen_k=16, head_dim=128, scale=0.125, causal=0, out_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_fwd_fp8_pv(*args.values())
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(v=0), INVALID, "v is NULL"),
+    (dict(codes=MIS), INVALID, "vt_codes is not 16-byte aligned"),
+    (dict(scales=0), INVALID, "block_scales is NULL"),
+    (dict(scales=CU_MIS), INVALID, "4-byte aligned"),
+    (dict(seqlen=0), INVALID, "sizes must be >= 1"),
+    (dict(in_dtype=0), UNSUP, "bf16"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
+    (dict(seqlen=1 << 24), INVALID, "below 2^31"),
+])
+def test_quantize_vt_fp8_argument_errors(lib, kw, code, text):
+    assert quantize_vt_fp8(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(vt=MIS), INVALID, "v is not 16-byte aligned"),
+    (dict(qs=0), INVALID, "q_scales is NULL"),
+    (dict(vs=0), INVALID, "v_scales is NULL"),
+    (dict(vs=CU_MIS), INVALID, "4-byte aligned"),
+    (dict(n_q_heads=3, n_kv_heads=2), INVALID, "multiple of n_kv_heads"),
+    (dict(causal=1, seqlen_k=17), UNSUP, "seqlen_q == seqlen_k"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
+])
+def test_fwd_fp8_pv_argument_errors(lib, kw, code, text):
+    assert fwd_fp8_pv(**kw) == code
+    assert text in binding.fa_last_error()
+
+
+def test_fp8_vt_bytes(lib):
+    assert binding.fa_fp8_vt_bytes(2, 3, 64, 128) == 2 * 3 * 64 * 128
+    assert binding.fa_fp8_vt_bytes(2, 3, 65, 64) == 2 * 3 * 128 * 64
+    assert binding.fa_fp8_vt_bytes(1, 1, 1, 128) == 64 * 128
+    assert binding.fa_fp8_vt_bytes(0, 3, 5, 64) == 0
+    assert binding.fa_fp8_vt_bytes(1, 1, -5, 64) == 0
 
 
 def test_fp8_scales_count(lib):

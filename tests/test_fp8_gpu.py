@@ -271,3 +271,162 @@ def test_fwd_fp8_incoherent_processing_lowers_the_error():
         errs[name] = float(np.sqrt(np.mean((host(o) - O_exact) ** 2)))
     print(f"rmse plain={errs['plain']:.4e} hadamard={errs['hadamard']:.4e} ratio={errs['plain'] / errs['hadamard']:.3f}")
     assert errs["hadamard"] < errs["plain"]
+
+
+# --- P V in FP8 (fa_quantize_vt_fp8, fa_fwd_fp8_pv) -------------------------
+
+def _vt_key_of(pos):
+    g, s = pos >> 5, pos & 31
+    return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * g + (s & 3)
+
+
+def _untranspose_vt(vt, N):
+    """[..., nb, d, 64] transposed codes -> [..., N, d] (keys in order)."""
+    *lead, nb, d, _ = vt.shape
+    keys = np.array([_vt_key_of(p) for p in range(64)])
+    out = np.zeros(tuple(lead) + (nb * 64, d), dtype=vt.dtype)
+    for j in range(nb):
+        out[..., j * 64 + keys, :] = np.swapaxes(vt[..., j, :, :], -1, -2)
+    return out[..., :N, :], out[..., N:, :]
+
+
+VT_CASES = [(2, 3, 200, 128, 0), (1, 2, 64, 64, 0), (1, 1, 1, 128, 0), (2, 2, 130, 64, 3), (1, 4, 333, 128, 2)]
+
+
+@pytest.mark.parametrize("case", VT_CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}o{c[4]}" for c in VT_CASES])
+def test_quantize_vt_fp8_bit_exact(case):
+    B, H, N, d, outl = case
+    announce(f"fa_quantize_vt_fp8 {case}")
+    inp = gen(51 + N, B, H, H, N, N, d, outliers=outl)
+    _, _, v, _ = upload(inp)
+    vt, vs = binding.quantize_vt_fp8(v)
+    codes, tail = _untranspose_vt(vt.cpu().numpy(), N)
+    oc, osc = ofp8.quantize(inp.v)
+    np.testing.assert_array_equal(vs.cpu().numpy(), osc.astype(np.float32))
+    np.testing.assert_array_equal(codes, oc)
+    assert np.all(tail == 0), "keys past the end must get code 0"
+
+
+def test_quantize_vt_fp8_ties_subnormals_and_extreme_blocks():
+    # the blocks of the Q/K quantize test, now as V (no transform either way)
+    d, N = 64, 4 * 64 + 1
+    x = np.zeros((1, 1, N, d), dtype=np.float32)
+    ties = np.array([448, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -5 * 2.0 ** -10, 2.0 ** -6 + 2.0 ** -10,
+                     15 * 2.0 ** -4 + 2.0 ** -5, 240 + 8, 2.0 ** -11, 0.0], dtype=np.float32)
+    rng = np.random.default_rng(9)
+    x[0, 0, :64] = rng.choice(ties, size=(64, d))
+    x[0, 0, 0, 0] = 448.0
+    mag = rng.uniform(2.0 ** -119, 1.5 * 2.0 ** -118, (64, d)) * rng.choice([-1.0, 1.0], (64, d))
+    x[0, 0, 128:192] = mag.astype(np.float32)
+    x[0, 0, 192:256] = rng.standard_normal((64, d)).astype(np.float32) * np.float32(1e30)
+    x[0, 0, 256] = -0.0
+    x = round_to_bf16(x)[0]
+    announce("fa_quantize_vt_fp8 ties/subnormals/extreme blocks")
+    vt, vs = binding.quantize_vt_fp8(_bf16_dev(x))
+    codes, _ = _untranspose_vt(vt.cpu().numpy(), N)
+    oc, osc = ofp8.quantize(x)
+    np.testing.assert_array_equal(vs.cpu().numpy(), osc.astype(np.float32))
+    np.testing.assert_array_equal(codes, oc)
+
+
+def _pv_bounds(qv, kv, vv, vc, vs, scale, causal, delta, tile=64):
+    """Per query row of one head: the flip bound (codes of P that the kernel
+    may round the other way, since its P carries the relative error
+    e^(2 delta) - 1 of its scores plus fp32 rounding) and the window bound of
+    the FP8 P V products (64 terms each, every term off by less than
+    2^(E - 12), E = floor(log2 max |term|)), both in units of O, and the
+    largest |V|. qv, kv, vv: dequantized Q, K, V (one head); vc, vs: V codes
+    [Nk, d] and block scales; delta: the score bound of each row."""
+    Nq, Nk = qv.shape[0], kv.shape[0]
+    S = scale * (qv @ kv.T)
+    if causal:
+        S = np.where(np.arange(Nk)[None, :] > np.arange(Nq)[:, None], -np.inf, S)
+    m_fin = S.max(axis=1)
+    ell = np.exp(S - m_fin[:, None]).sum(axis=1)
+    vdec = ofp8.e4m3_decode(vc)  # V / 2^e
+    flip = np.zeros(Nq)
+    win = np.zeros(Nq)
+    m = np.full(Nq, -np.inf)
+    eps = np.expm1(2 * delta) + 2.0 ** -20
+    for t, j0 in enumerate(range(0, Nk, tile)):
+        cols = slice(j0, min(Nk, j0 + tile))
+        St = S[:, cols]
+        m = np.maximum(m, St.max(axis=1))
+        seen = m > -np.inf
+        Pt = np.where(seen[:, None], np.exp(St - np.where(seen, m, 0.0)[:, None]), 0.0) * 256.0  # kernel's P 2^8
+        w = np.where(seen, np.exp(np.where(seen, m - m_fin, 0.0)), 0.0) / ell  # weight of this tile in O
+        code = ofp8.e4m3_encode(np.clip(Pt, 0, 448))
+        val = ofp8.e4m3_decode(code)
+        lo = ofp8.e4m3_decode(np.maximum(code.astype(np.int64) - 1, 0).astype(np.uint8))
+        hi = ofp8.e4m3_decode(np.minimum(code.astype(np.int64) + 1, 0x7E).astype(np.uint8))
+        # distance to the nearer midpoint, relative to P
+        near = np.minimum(np.abs(Pt - (val + lo) / 2), np.abs(Pt - (val + hi) / 2)) <= eps[:, None] * Pt
+        step = np.maximum(val - lo, hi - val) / 256.0
+        vabs = np.abs(vv[cols]).max(axis=1)
+        flip += w * (near * step * vabs[None, :]).sum(axis=1)
+        # window of the FP8 product: terms P code x V code, per channel
+        terms = np.abs(val[:, :, None] * vdec[cols][None, :, :])  # [Nq, keys, d]
+        tmax = terms.max(axis=1)
+        E = np.floor(np.log2(np.where(tmax > 0, tmax, 1.0)))
+        per_c = np.where(tmax > 0, terms.shape[1] * np.exp2(E - 12), 0.0)  # [Nq, d]
+        win += w * per_c.max(axis=1) * vs[t] / 256.0
+    return flip, win
+
+
+PV_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, causal, with signs, outlier channels, scale, d)
+    (1, 4, 2, 300, 300, True, True, 4, None, 128),
+    (2, 2, 2, 130, 257, False, False, 0, None, 128),
+    (1, 2, 1, 1, 1, True, True, 0, None, 128),
+    (1, 2, 2, 200, 200, True, True, 2, -0.1, 128),
+    (1, 2, 1, 64, 64, False, True, 0, 0.0, 128),
+    (1, 1, 1, 1100, 1100, True, True, 0, None, 128),
+    (1, 4, 2, 300, 300, True, True, 4, None, 64),
+    (2, 2, 2, 130, 257, False, False, 0, None, 64),
+    (1, 2, 1, 200, 1000, False, True, 0, None, 64),
+]
+
+
+@pytest.mark.parametrize("case", PV_CASES, ids=[_fwd_id(c) for c in PV_CASES])
+def test_fwd_fp8_pv_parity(case):
+    # against the oracle's tiled P-in-FP8 forward on the dequantized Q, K, V,
+    # within the bf16 forward's bounds plus: the score window bound (as for
+    # fa_fwd_fp8), the codes of P that a score that far off can round the
+    # other way, and the window of the FP8 P V products
+    import torch
+    B, Hq, Hkv, Nq, Nk, causal, with_signs, outl, scale, d = case
+    scale = float(np.float32(1 / np.sqrt(d))) if scale is None else scale
+    announce(f"fa_fwd_fp8_pv {_fwd_id(case)}")
+    inp = gen(61 + Nq + Nk, B, Hq, Hkv, Nq, Nk, d, outliers=outl)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(7, d) if with_signs else None
+    dq_c, dq_s = binding.quantize_fp8(q, _signs_dev(signs))
+    dk_c, dk_s = binding.quantize_fp8(k, _signs_dev(signs))
+    vt, vs = binding.quantize_vt_fp8(v)
+    o32, lse = binding.forward_fp8_pv(dq_c, dq_s, dk_c, dk_s, vt, vs, scale, causal, out_dtype=torch.float32)
+    o16, lse16 = binding.forward_fp8_pv(dq_c, dq_s, dk_c, dk_s, vt, vs, scale, causal, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    oqc, oqs = ofp8.quantize(inp.q, signs)
+    okc, oks = ofp8.quantize(inp.k, signs)
+    ovc, ovs = ofp8.quantize(inp.v)
+    qd, kd, vd = ofp8.dequantize(oqc, oqs), ofp8.dequantize(okc, oks), ofp8.dequantize(ovc, ovs)
+    O, L = ofp8.forward_probs_fp8_online(qd, kd, vd, scale, causal, tile=64)
+    O32, L32, O16 = host(o32), host(lse), host(o16)
+    worst = (0.0, 0.0, 0.0)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            delta = window_bound(oqc[b, h], oqs[b, h], okc[b, g], oks[b, g], scale, causal)
+            flip, win = _pv_bounds(qd[b, h], kd[b, g], vd[b, g], ovc[b, g], ovs[b, g], scale, causal, delta)
+            vmax = np.max(np.abs(vd[b, g]))
+            dl = np.abs(L32[b, h] - L[b, h])
+            do = np.max(np.abs(O32[b, h] - O[b, h]), axis=-1)
+            assert np.all(dl <= 1e-3 + delta), f"L head {(b, h)}"
+            bound_o = 1e-2 + np.expm1(2 * delta) * vmax + flip + win
+            assert np.all(do <= bound_o), f"O head {(b, h)}: worst excess {np.max(do - bound_o):.3e}"
+            assert np.all(np.abs(O16[b, h] - O[b, h]) <= bound_o[:, None] + bf16_half_ulp(O[b, h])), f"bf16 O {(b, h)}"
+            worst = (max(worst[0], float(do.max())), max(worst[1], float(dl.max())), max(worst[2], float((flip + win).max())))
+    print(f"max|dO|={worst[0]:.3e} max|dL|={worst[1]:.3e} flip+window bound <= {worst[2]:.3e}")
+    if outl == 0:
+        assert worst[0] <= 1e-2 and worst[1] <= 1e-3
+    assert np.array_equal(host(lse16), L32), "L must not depend on the output dtype"
