@@ -187,7 +187,7 @@ def forward_probs_fp8(q, k, v, scale, causal):
     return O, L
 
 
-def forward_probs_fp8_online(q, k, v, scale, causal, tile=64, quant=None):
+def forward_probs_fp8_online(q, k, v, scale, causal, tile=64, quant=None, rows=None):
     """P in FP8 the way a tiled forward forms it: against the running row
     maximum of the key tiles seen so far (online softmax, page "6.2
     FlashAttention V2 chi tiết", section 6.1), so the rounding is applied to
@@ -198,15 +198,19 @@ def forward_probs_fp8_online(q, k, v, scale, causal, tile=64, quant=None):
         a = exp(m - m'),  P~_j = exp(S_j - m'),
         O = a O + fp8(P~_j) V_j,  l = a l + rowsum P~_j,  m = m'
     then O / l and L = m + ln l. `quant` replaces fp8 (identity: plain
-    attention). q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]; float64 results."""
+    attention); `rows` optionally selects query rows (their positions still
+    decide the causal mask). q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]; float64
+    results [B, Hq, len(rows) or Nq, ...]."""
     quant = quantize_probs if quant is None else quant
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
-    B, Hq, Nq, _ = q.shape
+    B, Hq, _, _ = q.shape
     G = Hq // k.shape[1]
     Nk = k.shape[2]
+    rows = np.arange(q.shape[2]) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = q[:, :, rows]
+    Nq = rows.size
     O = np.empty((B, Hq, Nq, v.shape[-1]))
     L = np.empty((B, Hq, Nq))
-    rows = np.arange(Nq)
     for b in range(B):
         for h in range(Hq):
             g = h // G

@@ -329,7 +329,7 @@ def test_quantize_vt_fp8_ties_subnormals_and_extreme_blocks():
     np.testing.assert_array_equal(codes, oc)
 
 
-def _pv_bounds(qv, kv, vv, vc, vs, scale, causal, delta, tile=64):
+def _pv_bounds(qv, kv, vv, vc, vs, scale, causal, delta, tile=64, rows=None):
     """Per query row of one head: the flip bound (codes of P that the kernel
     may round the other way, since its P carries the relative error
     e^(2 delta) - 1 of its scores plus fp32 rounding) and the window bound of
@@ -337,10 +337,12 @@ def _pv_bounds(qv, kv, vv, vc, vs, scale, causal, delta, tile=64):
     2^(E - 12), E = floor(log2 max |term|)), both in units of O, and the
     largest |V|. qv, kv, vv: dequantized Q, K, V (one head); vc, vs: V codes
     [Nk, d] and block scales; delta: the score bound of each row."""
+    rows = np.arange(qv.shape[0]) if rows is None else np.asarray(rows)
+    qv = qv[rows]
     Nq, Nk = qv.shape[0], kv.shape[0]
     S = scale * (qv @ kv.T)
     if causal:
-        S = np.where(np.arange(Nk)[None, :] > np.arange(Nq)[:, None], -np.inf, S)
+        S = np.where(np.arange(Nk)[None, :] > rows[:, None], -np.inf, S)
     m_fin = S.max(axis=1)
     ell = np.exp(S - m_fin[:, None]).sum(axis=1)
     vdec = ofp8.e4m3_decode(vc)  # V / 2^e
@@ -430,3 +432,45 @@ def test_fwd_fp8_pv_parity(case):
     if outl == 0:
         assert worst[0] <= 1e-2 and worst[1] <= 1e-3
     assert np.array_equal(host(lse16), L32), "L must not depend on the output dtype"
+
+
+def test_fwd_fp8_pv_outlier_workload_full_size():
+    # the GQA workload with outlier channels at full size through the FP8 P V
+    # path; sampled heads and rows against the oracle's tiled P-in-FP8
+    # forward, within the same bounds as the small cases
+    import torch
+    w = WORKLOADS["fwd_bf16_causal_gqa_b4_hq32_hkv8_n4096_d128_outliers"]
+    announce(f"fa_fwd_fp8_pv full size {w.name}")
+    inp = gen(w.seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim,
+              outliers=w.n_outlier_channels)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(w.seed, w.head_dim)
+    sd = _signs_dev(signs)
+    qc, qs = binding.quantize_fp8(q, sd)
+    kc, ks = binding.quantize_fp8(k, sd)
+    vt, vs = binding.quantize_vt_fp8(v)
+    o, lse = binding.forward_fp8_pv(qc, qs, kc, ks, vt, vs, w.scale, w.causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = host(o), host(lse)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    rng = np.random.default_rng(98)
+    worst_o = worst_l = 0.0
+    for b, h in [(0, 0), (2, 17), (3, w.n_q_heads - 1)]:
+        g = h // w.group
+        oqc, oqs = ofp8.quantize(inp.q[b, h], signs)
+        okc, oks = ofp8.quantize(inp.k[b, g], signs)
+        ovc, ovs = ofp8.quantize(inp.v[b, g])
+        codes, _ = _untranspose_vt(vt[b, g].cpu().numpy()[None, None], w.seqlen)
+        np.testing.assert_array_equal(codes[0, 0], ovc)
+        rows = _sample_rows(rng, w.seqlen, 48)
+        qd, kd, vd = ofp8.dequantize(oqc, oqs), ofp8.dequantize(okc, oks), ofp8.dequantize(ovc, ovs)
+        Or, Lr = ofp8.forward_probs_fp8_online(qd[None, None], kd[None, None], vd[None, None], w.scale, w.causal,
+                                               rows=rows)
+        delta = window_bound(oqc, oqs, okc, oks, w.scale, w.causal, rows)
+        flip, win = _pv_bounds(qd, kd, vd, ovc, ovs, w.scale, w.causal, delta, rows=rows)
+        dl = np.abs(L[b, h][rows] - Lr[0, 0])
+        do = np.max(np.abs(O[b, h][rows] - Or[0, 0]), axis=-1)
+        assert np.all(dl <= 1e-3 + delta), f"L head {(b, h)}"
+        assert np.all(do <= 1e-2 + np.expm1(2 * delta) * np.max(np.abs(vd)) + flip + win), f"O head {(b, h)}"
+        worst_o, worst_l = max(worst_o, float(do.max())), max(worst_l, float(dl.max()))
+    print(f"{w.name} fp8 P V: max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")

@@ -305,3 +305,8 @@ def test_online_probs_fp8_reduces_to_the_direct_definitions(causal):
     if causal:
         for h in range(2):
             np.testing.assert_array_equal(O4[0, h, 0], v[0, 0, 0])  # row 0: one key, P~ = 1 exactly
+    # selected rows keep their positions (and so their causal masks)
+    sel = np.array([0, 5, 64, 149])
+    O5, L5 = fp8.forward_probs_fp8_online(q, k, v, 0.3, causal, tile=64, rows=sel)
+    np.testing.assert_array_equal(O5, O4[:, :, sel])
+    np.testing.assert_array_equal(L5, L4[:, :, sel])
