@@ -134,6 +134,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known to be wave-uniform
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int j16 = lane & 15;
@@ -218,17 +219,17 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     const int hq = hkv * a.G + hm;
     const size_t qhead = (size_t)(b * a.Hq + hq) * a.Nq;
     const int q0 = i * BQ;
-    const char* Qh = (const char*)a.q + qhead * QROWB;
-    const char* Oh = (const char*)a.dout + qhead * QROWB;
+    const char* Qb = uniform_ptr((const char*)a.q + (qhead + q0) * QROWB);
+    const char* Ob = uniform_ptr((const char*)a.dout + (qhead + q0) * QROWB);
 #pragma unroll
     for (int u = 0; u < QCPW; ++u) {
-      const int cb = (w * QCPW + u) * 64;
+      const int cb = (wu * QCPW + u) * 64;
       const int idx = cb + lane;
       const int row = idx / QRC, pc = idx % QRC;
       const int lc = pc ^ swz<QRC>(row);
-      const size_t off = (size_t)min(q0 + row, a.Nq - 1) * QROWB + lc * 16;
-      load_lds_16(Qh + off, sQ + buf * QTILEB + cb * 16);
-      load_lds_16(Oh + off, sDO + buf * QTILEB + cb * 16);
+      const unsigned off = (unsigned)(min(row, a.Nq - 1 - q0) * QROWB + lc * 16);
+      load_lds_16(Qb, off, sQ + buf * QTILEB + cb * 16);
+      load_lds_16(Ob, off, sDO + buf * QTILEB + cb * 16);
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < a.Nq;
@@ -471,6 +472,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known to be wave-uniform
   const int kg = w & 3;  // key group: keys 32*kg.. of the block
   const int h = w >> 2;  // query half for S and dP, head-dim half for dK and dV
   const int g = lane >> 5;
@@ -577,14 +579,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int last = Nq - 1 - q0;
 #pragma unroll
     for (int u = 0; u < QCPW; ++u) {
-      const int cb = (w * QCPW + u) * 64;
+      const int cb = (wu * QCPW + u) * 64;
       const int idx = cb + lane;
       const int row = idx / RC, pc = idx % RC;
       const int lc = pc ^ swz<RC>(row);
       unsigned off = (unsigned)(min(row, last) * ROWB + lc * 16);
       asm volatile("" : "+v"(off));
-      load_lds_16(Qb + off, nQ + cb * 16);
-      load_lds_16(Ob + off, nDO + cb * 16);
+      load_lds_16(Qb, off, nQ + cb * 16);
+      load_lds_16(Ob, off, nDO + cb * 16);
     }
   };
   auto store_ld = [&](float* nL, float* nD) __attribute__((always_inline)) {
@@ -870,6 +872,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known to be wave-uniform
   const int G = lane >> 4;  // lane group of the 16x16x32 layouts
   const int n16 = lane & 15;
 
@@ -965,14 +968,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int last = Nq - 1 - q0;
 #pragma unroll
     for (int u = 0; u < QCPW; ++u) {
-      const int cb = (w * QCPW + u) * 64;
+      const int cb = (wu * QCPW + u) * 64;
       const int idx = cb + lane;
       const int row = idx / RC, pc = idx % RC;
       const int lc = pc ^ dkdv4_swz<RC>(row);
       unsigned off = (unsigned)(min(row, last) * ROWB + lc * 16);
       asm volatile("" : "+v"(off));
-      load_lds_16(Qb + off, nQ + cb * 16);
-      load_lds_16(Ob + off, nDO + cb * 16);
+      load_lds_16(Qb, off, nQ + cb * 16);
+      load_lds_16(Ob, off, nDO + cb * 16);
     }
   };
   auto store_ld = [&](float* nL, float* nD) __attribute__((always_inline)) {
@@ -1119,6 +1122,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the same value, known to be wave-uniform
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int j16 = lane & 15;
@@ -1214,32 +1218,32 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   int ldoff[NP];
 #pragma unroll
   for (int h = 0; h < NP; ++h) {
-    const int idx = (w * CPW + h) * 64 + lane;
+    const int idx = (wu * CPW + h) * 64 + lane;
     const int row = idx / RC;
     ldoff[h] = row * ROWB + (((idx % RC) ^ swz<RC>(row)) << 4);
   }
   auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
     const int kv0 = jt * BC;
+    const char* Kb = uniform_ptr(Kh + (size_t)kv0 * ROWB);
+    const char* Vb = uniform_ptr(Vh + (size_t)kv0 * ROWB);
     if (kv0 + BC <= Nk) {
-      const char* Kb = Kh + (size_t)kv0 * ROWB;
-      const char* Vb = Vh + (size_t)kv0 * ROWB;
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
-        const int cb = (w * CPW + u) * 64;
-        const int off = ldoff[u % NP] + (u / NP) * NP * RPL * ROWB;
-        load_lds_16(Kb + off, Kt + cb * 16);
-        load_lds_16(Vb + off, Vt + cb * 16);
+        const int cb = (wu * CPW + u) * 64;
+        const unsigned off = (unsigned)(ldoff[u % NP] + (u / NP) * NP * RPL * ROWB);
+        load_lds_16(Kb, off, Kt + cb * 16);
+        load_lds_16(Vb, off, Vt + cb * 16);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
-        const int cb = (w * CPW + u) * 64;
+        const int cb = (wu * CPW + u) * 64;
         const int idx = cb + lane;
         const int row = idx / RC, pc = idx % RC;
         const int lc = pc ^ swz<RC>(row);
-        const size_t off = (size_t)min(kv0 + row, Nk - 1) * ROWB + lc * 16;
-        load_lds_16(Kh + off, Kt + cb * 16);
-        load_lds_16(Vh + off, Vt + cb * 16);
+        const unsigned off = (unsigned)(min(row, Nk - 1 - kv0) * ROWB + lc * 16);
+        load_lds_16(Kb, off, Kt + cb * 16);
+        load_lds_16(Vb, off, Vt + cb * 16);
       }
     }
   };

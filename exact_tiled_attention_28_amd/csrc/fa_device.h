@@ -130,12 +130,22 @@ __device__ __forceinline__ bf16x8 cat4(short4v a, short4v b) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// HBM -> LDS without registers (global_load_lds_dwordx4): every lane fetches
-// 16 bytes from its own global address; lane l's bytes land at
-// lds_wave_base + 16*l (checked on gfx950). lds_wave_base must be uniform
-// across the wavefront.
-__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_wave_base, 16, 0, 0);
+// Word 3 of a raw buffer resource on gfx950 (as on the other gfx9 parts):
+// 32-bit data format, no swizzle; with stride 0 the resource is a plain
+// byte-addressed range of num_records bytes.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// HBM -> LDS without registers, through a buffer resource
+// (buffer_load_dwordx4 ... lds): lane l fetches the 16 bytes at byte offset
+// voff from base into lds_wave_base + 16*l. base and lds_wave_base must be
+// uniform across the wavefront (base in scalar registers, see uniform_ptr).
+// The buffer form rather than global_load_lds_dwordx4: the compiler treats
+// the global form as an access that may reach LDS through the flat address
+// space and, while one is in flight, waits for every LDS read before using
+// any (lgkmcnt(0)); with the buffer form it counts LDS reads in order.
+__device__ __forceinline__ void load_lds_16(const char* base, unsigned voff, void* lds_wave_base) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, kRawBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_wave_base, 16, voff, 0, 0, 0);
 }
 
 // The same pointer, read from the first active lane into scalar registers

@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       unsigned ou = (unsigned)ld[u];
       if (!FULL && rowb != 0 && kv0 + BC > Nk && ou / rowb > last) ou = last * rowb + ou % rowb;
       asm volatile("" : "+v"(ou));
-      load_lds_16(Xb + ou, Xt + (wu * CPWX + u) * 64 * 16);
+      load_lds_16(Xb, ou, Xt + (wu * CPWX + u) * 64 * 16);
     }
   };
   auto issue_k = [&](auto full_tag, int jt, char* Kt) __attribute__((always_inline)) {

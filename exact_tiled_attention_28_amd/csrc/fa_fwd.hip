@@ -180,15 +180,15 @@ fwd_kernel(FwdArgs a) {
     }
     auto issue_tile = [&](int jt, char* Kt, char* Vt) __attribute__((always_inline)) {
       const int kv0 = jt * BC;
+      const char* Kb = uniform_ptr(Kh + (size_t)kv0 * ROWB);
+      const char* Vb = uniform_ptr(Vh + (size_t)kv0 * ROWB);
       if (kv0 + BC <= Nk) {
-        const char* Kb = Kh + (size_t)kv0 * ROWB;
-        const char* Vb = Vh + (size_t)kv0 * ROWB;
   #pragma unroll
         for (int u = 0; u < CPW; ++u) {
           const int cb = (wu * CPW + u) * 64;
           const unsigned off = (unsigned)(ldoff[u % NP] + (u / NP) * NP * RPL * ROWB);
-          load_lds_16(Kb + off, Kt + cb * 16);
-          load_lds_16(Vb + off, Vt + cb * 16);
+          load_lds_16(Kb, off, Kt + cb * 16);
+          load_lds_16(Vb, off, Vt + cb * 16);
         }
       } else {
   #pragma unroll
@@ -197,17 +197,16 @@ fwd_kernel(FwdArgs a) {
           const int idx = cb + lane;
           const int row = idx / RC, pc = idx % RC;
           const int lc = pc ^ swz<RC>(row);
-          const int grow = min(kv0 + row, Nk - 1);
-          const size_t off = (size_t)grow * ROWB + lc * 16;
-          load_lds_16(Kh + off, Kt + cb * 16);
-          load_lds_16(Vh + off, Vt + cb * 16);
+          const unsigned off = (unsigned)(min(row, Nk - 1 - kv0) * ROWB + lc * 16);
+          load_lds_16(Kb, off, Kt + cb * 16);
+          load_lds_16(Vb, off, Vt + cb * 16);
         }
       }
     };
 
     // One tile (K or V, from head base Xh) into Xt. Each load is the tile's
-    // scalar base plus the lane's 32-bit offset (global_load_lds_dwordx4 with
-    // a scalar address): the tile base is made opaque, and so is the offset
+    // scalar base plus the lane's 32-bit offset (a buffer load whose resource
+    // holds the tile base): the tile base is made opaque, and so is the offset
     // right before its use, so that neither is folded into per-lane 64-bit
     // pointers kept live across the loop. In a tile that runs past the end of
     // K/V, rows past the end read the last row instead (their scores are
@@ -230,7 +229,7 @@ fwd_kernel(FwdArgs a) {
       for (int u = 0; u < CPW; ++u) {
         unsigned ou = o[u];
         asm volatile("" : "+v"(ou));
-        load_lds_16(Xb + ou, Xt + (wu * CPW + u) * 64 * 16);
+        load_lds_16(Xb, ou, Xt + (wu * CPW + u) * 64 * 16);
       }
     };
 
