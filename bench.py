@@ -641,9 +641,10 @@ def csrc_sha256():
 # whether it also zeroes dQ: only fa_bwd_atomic's does).
 CALL_KERNELS = {
     "fa_fwd": ("void fa::fwd_kernel<",),
-    "fa_bwd": ("void fa::bwd_dkdv_kernel<", "void fa::bwd_dq_kernel<"),
+    "fa_bwd": ("void fa::bwd_dkdv_kernel<", "void fa::bwd_dkdv4_kernel<", "void fa::bwd_dq_kernel<"),
     "fa_bwd_atomic": ("void fa::bwd_kernel<",),
     "fa_quantize_fp8": ("void fa::quantize_fp8_kernel<",),
+    "fa_quantize_vt_fp8": ("void fa::quantize_vt_fp8_kernel<",),
     "fa_fwd_fp8": ("void fa::fwd_fp8_kernel<",),
 }
 
@@ -655,19 +656,25 @@ def _template_args(kernel):
     return [t.strip() for t in kernel[kernel.index("<") + 1:kernel.rindex(">(")].split(",")]
 
 
-# Position of the VARLEN / PERSIST template argument of each kernel template
+# Position of the VARLEN / PERSIST / PV8 template argument of each kernel template
 # (fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>,
-# bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN, HILO>, bwd_dq_kernel<D, CAUSAL, VARLEN, NW, HILO>).
+# bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN, HILO>, bwd_dkdv4_kernel<D, CAUSAL, GF32, VARLEN>,
+# bwd_dq_kernel<D, CAUSAL, VARLEN, NW, HILO>, fwd_fp8_kernel<D, CAUSAL, OUTF32, PV8>).
 _VARLEN_ARG = {
     "void fa::fwd_kernel<": 5,
     "void fa::bwd_dkdv_kernel<": 3,
+    "void fa::bwd_dkdv4_kernel<": 3,
     "void fa::bwd_dq_kernel<": 2,
 }
 _PERSIST_ARG = {"void fa::fwd_kernel<": 6}
+_PV8_ARG = {"void fa::fwd_fp8_kernel<": 3}
 
 
 def _call_of(kernel):
     t = _template_args(kernel)
+    for prefix, pos in _PV8_ARG.items():
+        if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
+            return "fa_fwd_fp8_pv"
     for prefix, pos in _PERSIST_ARG.items():
         if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
             return "fa_fwd_persistent"

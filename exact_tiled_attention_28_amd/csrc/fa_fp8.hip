@@ -32,26 +32,26 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 // ---------------------------------------------------------------------------
 // e4m3 (OCP FP8 E4M3FN: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
-// largest finite 448, subnormal step 2^-9) code of |v| <= 448, round to
-// nearest, ties to even.
+// largest finite 448, subnormal step 2^-9) codes of four values with
+// |v| <= 448, round to nearest, ties to even, packed into one word (value j
+// in byte j): gfx950's v_cvt_pk_fp8_f32 converts two fp32 values into two
+// bytes of a word with exactly this rounding (checked bit for bit on
+// [-448, 448] against the E4M3 definition, ties, subnormals, fp32 subnormals
+// and signed zeros included).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned e4m3_code(float v) {
-  const unsigned sign = __float_as_uint(v) >> 31;
-  const float a = fabsf(v);
-  unsigned mag;
-  if (a >= 0.015625f) {  // 2^-6: normal range
-    // Keep 3 of the 23 fp32 mantissa bits, rounding the dropped 20 bits to
-    // nearest even; a carry out of the mantissa bumps the exponent, which is
-    // what the encoding needs.
-    const unsigned u = __float_as_uint(a);
-    const unsigned r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // (biased fp32 exponent << 3) | m3
-    mag = r - ((127u - 7u) << 3);
-  } else {
-    // Subnormal: a / 2^-9 rounded to nearest even integer (0..8; 8 is the
-    // smallest normal, code 0x08).
-    mag = (unsigned)__builtin_rintf(a * 512.0f);
-  }
-  return (sign << 7) | mag;
+__device__ __forceinline__ unsigned e4m3_word(float v0, float v1, float v2, float v3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+  return (unsigned)w;
+}
+
+// The value of v in lane l ^ M (M = 1 or 2) of the same 4-lane quad: a DPP
+// quad permutation, a plain vector move with no LDS round trip.
+template <int M>
+__device__ __forceinline__ float quad_xor(float v) {
+  static_assert(M == 1 || M == 2, "within a quad");
+  constexpr int kQuadPerm = M == 1 ? 0xB1 : 0x4E;  // lanes (1,0,3,2) or (2,3,0,1)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadPerm, 0xF, 0xF, false));
 }
 
 // Exponent e of the smallest power of two with amax <= 448 * 2^e (amax > 0,
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(256) quantize_fp8_kernel(const __bf16* __restr
       const bool lower = (q & m) == 0;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float o = __shfl_xor(v[e], m, 64);
+        const float o = m == 1 ? quad_xor<1>(v[e]) : quad_xor<2>(v[e]);
         v[e] = lower ? v[e] + o : o - v[e];
       }
     }
@@ -151,10 +151,8 @@ __global__ void __launch_bounds__(256) quantize_fp8_kernel(const __bf16* __restr
       u32x4 out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        unsigned word = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(v[16 * u + 4 * i + j], -e2)) << (8 * j);
-        out[i] = word;
+        const float* t = v + 16 * u + 4 * i;
+        out[i] = e4m3_word(ldexpf(t[0], -e2), ldexpf(t[1], -e2), ldexpf(t[2], -e2), ldexpf(t[3], -e2));
       }
       *(u32x4*)(cr + 16 * u) = out;
     }
@@ -238,13 +236,10 @@ __global__ void __launch_bounds__(256) quantize_vt_fp8_kernel(const __bf16* __re
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      unsigned word = 0;
+      float t[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = (float)tile[vt_key_of(p0 + 4 * i + j) * D + c];
-        word |= e4m3_code(ldexpf(v, -e2)) << (8 * j);
-      }
-      o[i] = word;
+      for (int j = 0; j < 4; ++j) t[j] = ldexpf((float)tile[vt_key_of(p0 + 4 * i + j) * D + c], -e2);
+      o[i] = e4m3_word(t[0], t[1], t[2], t[3]);
     }
     *(u32x4*)(out + c * 64 + p0) = o;
   }

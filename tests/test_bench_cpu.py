@@ -38,6 +38,15 @@ def test_kernel_to_entry_point():
     assert bench._call_of("_ZN2fa21bwd_preprocess_kernelILi128ELb0ELb0EEEvPKDF16bPKvPfS5_x") == "fa_bwd"
     assert bench._call_of("_ZN2fa21bwd_preprocess_kernelILi128ELb0ELb1EEEvPKDF16bPKvPfS5_x") == "fa_bwd_atomic"
     assert bench._call_of("__amd_rocclr_copyBuffer") is None
+    # the d=64 dK/dV pass, the FP8 P V forward and the transposed V quantizer
+    assert bench._call_of("void fa::bwd_dkdv4_kernel<64, true, false, false>(fa::BwdArgs)") == "fa_bwd"
+    assert bench._call_of("void fa::bwd_dkdv4_kernel<64, true, false, true>(fa::BwdArgs)") == "fa_bwd_varlen"
+    assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, false>(fa::FwdArgs)") == "fa_fwd_fp8"
+    assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, true>(fa::FwdArgs)") == "fa_fwd_fp8_pv"
+    assert bench._call_of("void fa::quantize_vt_fp8_kernel<128>(bool _Accum const*, unsigned char*, float*, int, "
+                          "int)") == "fa_quantize_vt_fp8"
+    assert bench._call_of("void fa::quantize_fp8_kernel<128>(bool _Accum const*, unsigned char*, float*, "
+                          "signed char const*, int, int)") == "fa_quantize_fp8"
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, true>(fa::FwdArgs)") == "fa_fwd_varlen"
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false>(fa::FwdArgs)") == "fa_fwd"
     assert bench._call_of("void fa::fwd_kernel<false, 128, true, false, 4, false, false>(fa::FwdArgs)") == "fa_fwd"

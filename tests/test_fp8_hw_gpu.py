@@ -99,10 +99,11 @@ def test_fp8_instruction_error_is_within_the_window_bound():
 
 
 def test_cvt_pk_fp8_rounds_like_the_e4m3_definition():
-    # v_cvt_pk_fp8_f32 (which the FP8 forward uses to pack P) against the
-    # oracle's E4M3 encoding on [0, 448]: every value, every midpoint between
-    # neighbours (ties to even), the fp32 neighbours of each midpoint, the
-    # subnormal range and random values; bit-exact.
+    # v_cvt_pk_fp8_f32 (which the FP8 forward uses to pack P and the
+    # quantize passes use for every code) against the oracle's E4M3 encoding
+    # on [-448, 448]: every value, every midpoint between neighbours (ties to
+    # even), the fp32 neighbours of each midpoint, the subnormal range, fp32
+    # subnormals, signed zeros and random values; bit-exact.
     import torch
     lib = ctypes.CDLL(LIB)
     lib.fp8_cvt_probe.restype = ctypes.c_int
@@ -117,6 +118,9 @@ def test_cvt_pk_fp8_rounds_like_the_e4m3_definition():
                         (rng.uniform(0, 2.0 ** -5, 4000)).astype(np.float32),
                         np.exp2(rng.uniform(-14, 8, 4000)).astype(np.float32)])
     x = np.clip(x, 0, 448).astype(np.float32)
+    # fp32 subnormals (the quantizers can scale a value of a block with a
+    # tiny maximum into that range): they encode as a signed zero
+    x = np.concatenate([x, np.array([1.4e-45, 1e-42, 1e-40, 1.1e-38], dtype=np.float32)])
     x = np.concatenate([x, -x])
     x = np.concatenate([x, np.zeros((-len(x)) % 4, dtype=np.float32)])
     announce(f"v_cvt_pk_fp8_f32 on {len(x)} values")
