@@ -618,8 +618,9 @@ fwd_kernel(FwdArgs a) {
 constexpr int kWide8MinKeys = 16384;
 // Without the causal mask the 8-wavefront kernel runs from this many keys
 // on: measured at d = 128 3.6 % faster at 8K, 5 % at 16K, 2-5 % at 32K (MHA
-// and GQA), level at 4K; at d = 64 5 % faster at 8K and 16K, 2.3 % at 32K.
-constexpr int kWide8MinKeysNonCausal = 8192;
+// and GQA), and with the buffer-form tile loads 4.1 % faster at 4K; at
+// d = 64 5 % faster at 8K and 16K, 2.3 % at 32K, 1 % at 4K.
+constexpr int kWide8MinKeysNonCausal = 4096;
 
 template <bool F32IN, int D, bool CAUSAL, bool OUTF32>
 static hipError_t launch_fwd_t(FwdArgs a, hipStream_t stream) {

@@ -122,7 +122,7 @@ LONG_CASES = [
     (1, 2, 2, 4100, 4100, 64, True),
     (1, 2, 1, 333, 4200, 128, False),
     (1, 1, 1, 4096, 4096, 64, False),
-    # 8-wavefront kernel without the causal mask (from 8192 keys): ragged
+    # 8-wavefront kernel without the causal mask (from 4096 keys): ragged
     # 256-row Q tiles and a ragged last K/V tile, MHA and GQA
     (1, 1, 1, 300, 8300, 128, False),
     (1, 4, 1, 520, 8200, 128, False),
