@@ -544,8 +544,9 @@ def bench_fp8(args):
     """Time the FP8 forward path on one forward workload: fa_quantize_fp8 of
     Q and of K (random-sign Hadamard transform, seed = the workload's) and
     fa_fwd_fp8 (bf16 O), with fa_fwd on the same inputs beside it, then
-    fa_quantize_vt_fp8 of V and fa_fwd_fp8_pv (P V in FP8 too). Prints one
-    JSON line. The roofline of fa_fwd_fp8 counts S = Q K^T at the fp8 peak
+    fa_quantize_vt_fp8 of V and fa_fwd_fp8_pv (P V in FP8 too), and
+    fa_fwd_fp8_quantize_q (Q quantized inside the forward) with either V.
+    Prints one JSON line. The roofline of fa_fwd_fp8 counts S = Q K^T at the fp8 peak
     and O = P V at the bf16 peak (half of the flops each); that of
     fa_fwd_fp8_pv counts both at the fp8 peak."""
     import torch
@@ -583,8 +584,16 @@ def bench_fp8(args):
     def fwd8pv():
         binding.forward_fp8_pv(qc, qs, kc, ks, vt, vs, w.scale, w.causal, o=o, lse=lse, stream=stream)
 
-    _, per_call, _ = time_calls(None, [quant_q, quant_k, fwd8, step.fwd, quant_v, fwd8pv], args.steps, args.warmup)
-    med = [float(np.median(per_call[:, i])) for i in range(6)]
+    def fwd8q():
+        binding.forward_fp8_quantize_q(q, kc, ks, v, w.scale, w.causal, signs=signs, o=o, lse=lse, stream=stream)
+
+    def fwd8qpv():
+        binding.forward_fp8_quantize_q(q, kc, ks, vt, w.scale, w.causal, signs=signs, v_scales=vs, o=o, lse=lse,
+                                       stream=stream)
+
+    _, per_call, _ = time_calls(None, [quant_q, quant_k, fwd8, step.fwd, quant_v, fwd8pv, fwd8q, fwd8qpv], args.steps,
+                                args.warmup)
+    med = [float(np.median(per_call[:, i])) for i in range(8)]
     avgpv = float(np.mean(per_call[:, 5]))
     avg8 = float(np.mean(per_call[:, 2]))
     ff = fwd_flops(w.batch, w.n_q_heads, w.seqlen, w.seqlen, w.head_dim, w.causal)
@@ -603,6 +612,12 @@ def bench_fp8(args):
            "quantize_vt_ms": round(med[4], 4),
            "fwd_fp8_pv_ms": round(med[5], 4), "fwd_fp8_pv_tflops": round(ff / (med[5] * 1e-3) / 1e12, 2),
            "fp8_pv_path_ms": round(med[0] + med[1] + med[4] + med[5], 4),
+           "fwd_fp8_quantize_q_ms": round(med[6], 4),
+           "fwd_fp8_quantize_q_tflops": round(ff / (med[6] * 1e-3) / 1e12, 2),
+           "fwd_fp8_quantize_q_pv_ms": round(med[7], 4),
+           "fwd_fp8_quantize_q_pv_tflops": round(ff / (med[7] * 1e-3) / 1e12, 2),
+           "fp8_fused_q_path_ms": round(med[1] + med[6], 4),
+           "fp8_fused_q_pv_path_ms": round(med[1] + med[4] + med[7], 4),
            "roofline_fp8_pv": {"kernel": "fa_fwd_fp8_pv (fwd_fp8_kernel, P V in FP8)", "bound": "mfma",
                                "achieved": round(ff / (avgpv * 1e-3) / 1e12, 2), "peak": MI355X_FP8_PEAK_TFLOPS,
                                "unit": "TFLOP/s",

@@ -91,6 +91,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.fa_fp8_vt_bytes.argtypes = [_c_int] * 4
         lib.fa_fwd_fp8_pv.restype = _c_int
         lib.fa_fwd_fp8_pv.argtypes = [_c_ptr] * 8 + [_c_int] * 6 + [_c_float] + [_c_int] * 2 + [_c_ptr]
+    if hasattr(lib, "fa_fwd_fp8_quantize_q"):
+        lib.fa_fwd_fp8_quantize_q.restype = _c_int
+        lib.fa_fwd_fp8_quantize_q.argtypes = [_c_ptr] * 8 + [_c_int] * 6 + [_c_float] + [_c_int] * 2 + [_c_ptr]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [_c_int] * 3
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -181,6 +184,13 @@ def fa_quantize_vt_fp8(v, vt_codes, block_scales, batch, n_heads, seqlen, head_d
 
 def fa_fp8_vt_bytes(batch, n_heads, seqlen, head_dim) -> int:
     return load_library().fa_fp8_vt_bytes(batch, n_heads, seqlen, head_dim)
+
+
+def fa_fwd_fp8_quantize_q(q, q_signs, k_codes, k_scales, v, v_scales, o, lse, batch, n_q_heads, n_kv_heads, seqlen_q,
+                          seqlen_k, head_dim, scale, causal, out_dtype, stream) -> int:
+    return load_library().fa_fwd_fp8_quantize_q(q, q_signs, k_codes, k_scales, v, v_scales, o, lse, batch, n_q_heads,
+                                                n_kv_heads, seqlen_q, seqlen_k, head_dim, scale, causal, out_dtype,
+                                                stream)
 
 
 def fa_fwd_fp8_pv(q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, o, lse, batch, n_q_heads, n_kv_heads,
@@ -451,4 +461,35 @@ def forward_fp8_pv(q_codes, q_scales, k_codes, k_scales, vt_codes, v_scales, sca
                        vt_codes.data_ptr(), v_scales.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
                        float(scale), int(bool(causal)), oc, _stream_handle(stream))
     _check(rc, "fa_fwd_fp8_pv")
+    return o, lse
+
+
+def forward_fp8_quantize_q(q, k_codes, k_scales, v, scale, causal, signs=None, v_scales=None, out_dtype=None, o=None,
+                           lse=None, stream=None):
+    """O, L of the FP8 forward with Q quantized inside the kernel: q is bf16
+    [B,Hq,Nq,d], k_codes / k_scales from quantize_fp8 (with the same signs),
+    v bf16 [B,Hkv,Nk,d] (v_scales None) or the transposed codes and scales of
+    quantize_vt_fp8. Equal bit for bit to quantize_fp8(q, signs) followed by
+    forward_fp8 / forward_fp8_pv."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k_codes.shape[1], k_codes.shape[2]
+    oc = FA_DTYPE_BF16 if out_dtype in (None, torch.bfloat16) else FA_DTYPE_F32
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=_torch_dtype(oc), device=q.device)
+    else:
+        oc = _dtype_code(o)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    tensors = (q, k_codes, k_scales, v, o, lse) + tuple(t for t in (signs, v_scales) if t is not None)
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if v_scales is not None and v.numel() != fa_fp8_vt_bytes(B, Hkv, Nk, d):
+        raise ValueError("the V codes must hold fa_fp8_vt_bytes(B, Hkv, Nk, d) bytes")
+    rc = fa_fwd_fp8_quantize_q(q.data_ptr(), signs.data_ptr() if signs is not None else None, k_codes.data_ptr(),
+                               k_scales.data_ptr(), v.data_ptr(), v_scales.data_ptr() if v_scales is not None else None,
+                               o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), oc,
+                               _stream_handle(stream))
+    _check(rc, "fa_fwd_fp8_quantize_q")
     return o, lse

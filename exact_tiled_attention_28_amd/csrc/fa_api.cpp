@@ -397,6 +397,43 @@ int fa_fwd_fp8_pv(const void* q_codes, const float* q_scales, const void* k_code
   return hip_status(e, "fa_fwd_fp8_pv launch");
 }
 
+int fa_fwd_fp8_quantize_q(const void* q, const signed char* q_signs, const void* k_codes, const float* k_scales,
+                          const void* v, const float* v_scales, void* o, float* lse, int batch, int n_q_heads,
+                          int n_kv_heads, int seqlen_q, int seqlen_k, int head_dim, float scale, int causal,
+                          int out_dtype, void* stream) {
+  std::string err;
+  int rc;
+  if ((rc = fa::check_fwd(q, k_codes, v, o, lse, fa::Shape{batch, n_q_heads, n_kv_heads, seqlen_q, seqlen_k, head_dim},
+                          scale, causal, FA_DTYPE_BF16, out_dtype, err)))
+    return fail(rc, err);
+  if (k_scales == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "k_scales is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "k_scales / v_scales must be 4-byte aligned");
+  if (v_scales != nullptr &&
+      (long long)batch * n_kv_heads * (((long long)seqlen_k + 63) / 64) * 64 * head_dim >= (1LL << 40))
+    return fail(FA_ERR_INVALID_ARGUMENT, "vt_codes too large");
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k_codes;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.G = n_q_heads / n_kv_heads;
+  a.Nq = seqlen_q;
+  a.Nk = seqlen_k;
+  a.c = std::fabs(scale) * 1.4426950408889634f;
+  a.neg = scale < 0.0f;
+  a.q_scales = nullptr;  // Q is quantized in the kernel
+  a.q_signs = q_signs;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  hipError_t e = fa::launch_fwd_fp8(a, head_dim, causal != 0, out_dtype == FA_DTYPE_F32, (hipStream_t)stream);
+  return hip_status(e, "fa_fwd_fp8_quantize_q launch");
+}
+
 size_t fa_fp8_scales_count(int batch, int n_heads, int seqlen) {
   if (batch <= 0 || n_heads <= 0 || seqlen <= 0) return 0;
   return (size_t)batch * (size_t)n_heads * (((size_t)seqlen + 63) / 64);

@@ -279,7 +279,14 @@ hipError_t launch_quantize_vt_fp8(const void* v, void* codes, float* scales, int
 // sum l stays in fp32 over the unrounded probabilities; the V block scale of
 // each tile is applied by keeping the accumulator in units of the current
 // tile's scale (a power-of-two rescale, skipped while the scale repeats).
-template <int D, bool CAUSAL, bool OUTF32, bool PV8 = false>
+// QBF16: Q arrives in bf16 and is quantized here, exactly as
+// fa_quantize_fp8 would (fa_fwd_fp8_quantize_q): each lane holds the head-dim
+// ranges [64 ks + 32 g, +32) of its query row that its Q operand needs, the
+// Hadamard butterflies run in the same stage order (h < 32 inside a range,
+// h = 32 between the two half-waves, h = 64 between a lane's two ranges), the
+// two wavefronts of a 64-row scale block exchange their maxima through LDS,
+// and the codes go straight into the operand registers.
+template <int D, bool CAUSAL, bool OUTF32, bool PV8 = false, bool QBF16 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_fp8_kernel(FwdArgs a) {
   constexpr int NW = 4, BR = 128, BC = 64, NKB = 2, NKS = D / 64, NDB = D / 32;
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
@@ -324,15 +331,100 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const char* __restrict__ Vh =
       uniform_ptr((const char*)a.v + (PV8 ? (size_t)(b * a.Hkv + hkv) * ceil_div(Nk, 64) * (D * 64) : kvhead * VROWB));
   const int nqb = ceil_div(Nq, 64), nkb = ceil_div(Nk, 64);
-  // A wavefront whose rows all lie past the end (last query tile) stores
-  // nothing; its block index is clamped to stay inside the scale array.
-  const float sq = a.q_scales[(size_t)(b * a.Hq + hq) * nqb + min(q0w >> 6, nqb - 1)];
   const float* __restrict__ sk = a.k_scales + (size_t)(b * a.Hkv + hkv) * nkb;
 
   // Q codes (B operand): 32 bytes of head-dim range [64 ks + 32 g, +32). A
   // negative scale flips the sign bit of every code (exact).
   i32x8 qf[NKS];
-  {
+  float sq;
+  if constexpr (QBF16) {
+    __shared__ float qmax[NW];
+    float v[NKS][32];
+    {
+      const __bf16* Qr = (const __bf16*)a.q + (qhead + qrow) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (qrow < Nq) x = *(const u32x4*)(Qr + 64 * ks + 32 * g + 8 * c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[ks][8 * c + 2 * i] = __uint_as_float(x[i] << 16);
+            v[ks][8 * c + 2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+          }
+        }
+    }
+    if (a.q_signs) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) v[ks][e] *= (float)a.q_signs[64 * ks + 32 * g + e];
+      // stages h = 1 .. 16 inside each 32-wide range
+#pragma unroll
+      for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 32; ++e)
+            if (!(e & h)) {
+              const float x0 = v[ks][e], x1 = v[ks][e + h];
+              v[ks][e] = x0 + x1;
+              v[ks][e + h] = x0 - x1;
+            }
+      // stage h = 32: element c of half-wave 0 with c + 32 of half-wave 1
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[ks][e]), __float_as_uint(v[ks][e]), false, false);
+          const float o = __uint_as_float(g ? r[0] : r[1]);
+          v[ks][e] = g ? o - v[ks][e] : v[ks][e] + o;
+        }
+      // stage h = 64 (d = 128): the lane's two ranges
+      if constexpr (NKS == 2) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const float x0 = v[0][e], x1 = v[1][e];
+          v[0][e] = x0 + x1;
+          v[1][e] = x0 - x1;
+        }
+      }
+      const float inv_sqrt_d = D == 64 ? 0.125f : 0.08838834764831845f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) v[ks][e] *= inv_sqrt_d;
+    }
+    // maximum over the 64-row block: this wavefront's 32 rows and those of
+    // wavefront w ^ 1 (rows past the end of Q are zeros, as in the pass)
+    float amax = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[ks][e]));
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    amax = half_swap_max(amax);
+    if (lane == 0) qmax[w] = amax;
+    __syncthreads();
+    const int e2 = block_scale_exp(fmaxf(qmax[w], qmax[w ^ 1]));
+    sq = ldexpf(1.0f, e2);
+    const unsigned sign = a.neg ? 0x80808080u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      unsigned wd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float* t = v[ks] + 4 * i;
+        wd[i] = e4m3_word(ldexpf(t[0], -e2), ldexpf(t[1], -e2), ldexpf(t[2], -e2), ldexpf(t[3], -e2)) ^ sign;
+      }
+      qf[ks] = i32x8{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], (int)wd[4], (int)wd[5], (int)wd[6], (int)wd[7]};
+    }
+  } else {
+    // A wavefront whose rows all lie past the end (last query tile) stores
+    // nothing; its block index is clamped to stay inside the scale array.
+    sq = a.q_scales[(size_t)(b * a.Hq + hq) * nqb + min(q0w >> 6, nqb - 1)];
     const char* Qr = (const char*)a.q + (qhead + qrow) * D;
     const unsigned sign = a.neg ? 0x80808080u : 0u;
 #pragma unroll
@@ -627,36 +719,45 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool PV8>
+template <int D, bool PV8, bool QBF16>
 static void launch_fwd_fp8_d(const FwdArgs& a, long long blocks, bool causal, bool out_f32, hipStream_t s) {
   if (causal) {
     if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true, PV8, QBF16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false, PV8, QBF16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {
     if (out_f32)
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true, PV8, QBF16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false, PV8>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false, PV8, QBF16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   }
+}
+
+template <int D, bool QBF16>
+static void launch_fwd_fp8_v(const FwdArgs& a, long long blocks, bool causal, bool out_f32, hipStream_t s) {
+  if (a.v_scales != nullptr)
+    launch_fwd_fp8_d<D, true, QBF16>(a, blocks, causal, out_f32, s);
+  else
+    launch_fwd_fp8_d<D, false, QBF16>(a, blocks, causal, out_f32, s);
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a0, int head_dim, bool causal, bool out_f32, hipStream_t s) {
   FwdArgs a = a0;
   a.n_q_tiles = ceil_div(a.Nq, 128);
   const long long blocks = (long long)a.B * a.Hq * a.n_q_tiles;
-  const bool pv8 = a.v_scales != nullptr;
+  // q_scales null: Q is bf16 and quantized in the kernel
+  const bool qbf16 = a.q_scales == nullptr;
   if (head_dim == 64) {
-    if (pv8)
-      launch_fwd_fp8_d<64, true>(a, blocks, causal, out_f32, s);
+    if (qbf16)
+      launch_fwd_fp8_v<64, true>(a, blocks, causal, out_f32, s);
     else
-      launch_fwd_fp8_d<64, false>(a, blocks, causal, out_f32, s);
+      launch_fwd_fp8_v<64, false>(a, blocks, causal, out_f32, s);
   } else {
-    if (pv8)
-      launch_fwd_fp8_d<128, true>(a, blocks, causal, out_f32, s);
+    if (qbf16)
+      launch_fwd_fp8_v<128, true>(a, blocks, causal, out_f32, s);
     else
-      launch_fwd_fp8_d<128, false>(a, blocks, causal, out_f32, s);
+      launch_fwd_fp8_v<128, false>(a, blocks, causal, out_f32, s);
   }
   return hipGetLastError();
 }

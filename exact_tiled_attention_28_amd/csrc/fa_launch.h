@@ -24,8 +24,11 @@ struct FwdArgs {
   int total_q, total_k;
   // FP8 forward (fa_fwd_fp8): q and k hold e4m3 codes; the power-of-two scale
   // of each 64-row block, [B][Hq][ceil(Nq/64)] and [B][Hkv][ceil(Nk/64)].
+  // q_scales null (fa_fwd_fp8_quantize_q): q is bf16, quantized in the
+  // kernel with the random signs q_signs [d] (null: no transform).
   const float* q_scales;
   const float* k_scales;
+  const signed char* q_signs;
   // FP8 P V (fa_fwd_fp8_pv): v holds the transposed codes of
   // fa_quantize_vt_fp8 and v_scales their block scales [B][Hkv][ceil(Nk/64)];
   // null for the bf16 V of fa_fwd_fp8.

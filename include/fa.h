@@ -315,6 +315,33 @@ int fa_fwd_fp8_pv(const void* q_codes, const float* q_scales, const void* k_code
                   int out_dtype, void* stream);
 
 /*
+ * fa_fwd_fp8_quantize_q — fa_fwd_fp8 (v_scales NULL) or fa_fwd_fp8_pv
+ * (v_scales given) with Q taken in bf16 and quantized inside the forward,
+ * exactly as fa_quantize_fp8 would with the same signs (the same butterflies
+ * in the same order, the same 64-row block scales, the same codes), so the
+ * outputs equal those of fa_quantize_fp8 followed by fa_fwd_fp8 /
+ * fa_fwd_fp8_pv bit for bit, without the separate pass over Q (FlashAttention-3
+ * news page, "Độ chính xác thấp FP8 và incoherent processing": the transform
+ * can be fused with the memory-bound work around it). Q's codes and scales
+ * are not written out.
+ *   q        device, bf16 [B][Hq][Nq][d], 16-byte aligned; finite
+ *   q_signs  device int8 [d] of +1 / -1 (the signs K was quantized with), or
+ *            NULL for no transform
+ *   k_codes, k_scales as in fa_fwd_fp8
+ *   v        bf16 [B][Hkv][Nk][d] if v_scales is NULL, else the transposed
+ *            codes of fa_quantize_vt_fp8 with their block scales v_scales
+ *   o, lse, scale, causal, out_dtype as in fa_fwd; head_dim 64 or 128.
+ * Errors as fa_fwd_fp8; k_scales NULL or a misaligned scale array is
+ * FA_ERR_INVALID_ARGUMENT. Asynchronous on stream.
+ */
+int fa_fwd_fp8_quantize_q(const void* q, const signed char* q_signs,
+                          const void* k_codes, const float* k_scales,
+                          const void* v, const float* v_scales, void* o,
+                          float* lse, int batch, int n_q_heads, int n_kv_heads,
+                          int seqlen_q, int seqlen_k, int head_dim, float scale,
+                          int causal, int out_dtype, void* stream);
+
+/*
  * fa_fwd_fp8 — fa_fwd with the scores formed in FP8: q_codes / k_codes and
  * q_scales / k_scales as written by fa_quantize_fp8 (with the same signs for
  * Q and K), S = scale * (Q_codes 2^e_q)(K_codes 2^e_k)^T by FP8 matrix cores

@@ -140,6 +140,16 @@ int main() {
                        128, 0.1f, 1, FA_DTYPE_F32, nullptr) == FA_OK);
   EXPECT(fa_fwd_fp8_pv(P, (const float*)P, P, (const float*)P, P, nullptr, P, (float*)P, 1, 2, 1, 64, 64, 128, 0.1f,
                        1, FA_DTYPE_F32, nullptr) == FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_fp8_quantize_q(P, nullptr, P, (const float*)P, P, nullptr, P, (float*)P, 1, 2, 1, 64, 64, 128, 0.1f,
+                               1, FA_DTYPE_BF16, nullptr) == FA_OK);
+  EXPECT(fa_fwd_fp8_quantize_q(P, (const signed char*)P, P, (const float*)P, P, (const float*)P, P, (float*)P, 1, 2,
+                               1, 64, 64, 64, -0.1f, 0, FA_DTYPE_F32, nullptr) == FA_OK);
+  EXPECT(fa_fwd_fp8_quantize_q(P, nullptr, P, nullptr, P, nullptr, P, (float*)P, 1, 2, 1, 64, 64, 128, 0.1f, 1,
+                               FA_DTYPE_BF16, nullptr) == FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_fp8_quantize_q(P, nullptr, P, (const float*)P, P, (const float*)(uintptr_t{0x10002}), P, (float*)P, 1,
+                               2, 1, 64, 64, 128, 0.1f, 1, FA_DTYPE_BF16, nullptr) == FA_ERR_INVALID_ARGUMENT);
+  EXPECT(fa_fwd_fp8_quantize_q(P, nullptr, P, (const float*)P, P, nullptr, P, (float*)P, 1, 2, 1, 64, 64, 96, 0.1f,
+                               1, FA_DTYPE_BF16, nullptr) == FA_ERR_UNSUPPORTED);
   EXPECT(fa_fwd_persistent(P, P, P, P, (float*)P, (int*)P, 1, 2, 1, 64, 64, 128, 0.1f, 1, FA_DTYPE_BF16,
                            FA_DTYPE_BF16, nullptr) == FA_OK);
   EXPECT(fa_fwd_persistent(P, P, P, P, (float*)P, (int*)(uintptr_t{0x10002}), 1, 2, 1, 64, 64, 128, 0.1f, 1,

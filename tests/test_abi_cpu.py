@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(
         ["fa_bwd", "fa_bwd_atomic", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fp8_scales_count",
-         "fa_fp8_vt_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_pv", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes",
+         "fa_fp8_vt_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_pv", "fa_fwd_fp8_quantize_q", "fa_fwd_persistent", "fa_fwd_persistent_sched_bytes",
          "fa_fwd_varlen", "fa_last_error", "fa_quantize_fp8", "fa_quantize_vt_fp8", "fa_status_string", "fa_version"])
 
 
@@ -491,3 +491,28 @@ def test_abi_under_host_sanitizers(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi driver ok" in r.stdout
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
+
+
+def fwd_fp8_quantize_q(**kw):
+    args = dict(q=P, signs=None, k=P, ks=CU, v=P, vs=None, o=P, lse=P, batch=1, n_q_heads=2, n_kv_heads=1,
+                seqlen_q=16, seqlen_k=16, head_dim=128, scale=0.125, causal=0, out_dtype=1, stream=None)
+    args.update(kw)
+    return binding.fa_fwd_fp8_quantize_q(*args.values())
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=0), INVALID, "q is NULL"),
+    (dict(q=MIS), INVALID, "q is not 16-byte aligned"),
+    (dict(v=MIS), INVALID, "v is not 16-byte aligned"),
+    (dict(ks=0), INVALID, "k_scales is NULL"),
+    (dict(ks=CU_MIS), INVALID, "4-byte aligned"),
+    (dict(vs=CU_MIS), INVALID, "4-byte aligned"),
+    (dict(n_q_heads=3, n_kv_heads=2), INVALID, "multiple of n_kv_heads"),
+    (dict(causal=1, seqlen_k=17), UNSUP, "seqlen_q == seqlen_k"),
+    (dict(out_dtype=9), INVALID, "FA_DTYPE"),
+    (dict(scale=float("nan")), INVALID, "scale must be finite"),
+    (dict(head_dim=96), UNSUP, "head_dim 96"),
+])
+def test_fwd_fp8_quantize_q_argument_errors(lib, kw, code, text):
+    assert fwd_fp8_quantize_q(**kw) == code
+    assert text in binding.fa_last_error()

@@ -474,3 +474,96 @@ def test_fwd_fp8_pv_outlier_workload_full_size():
         assert np.all(do <= 1e-2 + np.expm1(2 * delta) * np.max(np.abs(vd)) + flip + win), f"O head {(b, h)}"
         worst_o, worst_l = max(worst_o, float(do.max())), max(worst_l, float(dl.max()))
     print(f"{w.name} fp8 P V: max|dO|={worst_o:.3e} max|dL|={worst_l:.3e}")
+
+
+# fa_fwd_fp8_quantize_q: Q in bf16, quantized inside the forward
+QQ_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, causal, with signs, outlier channels, scale, d, P V in FP8)
+    (1, 4, 2, 300, 300, True, True, 4, None, 128, False),
+    (2, 2, 2, 130, 257, False, False, 0, None, 128, False),
+    (1, 2, 1, 1, 1, True, True, 0, None, 128, True),
+    (1, 2, 2, 200, 200, True, True, 2, -0.1, 128, True),
+    (1, 3, 1, 70, 600, False, True, 0, None, 64, False),
+    (1, 4, 2, 300, 300, True, True, 4, None, 64, True),
+    (1, 1, 1, 1100, 1100, True, True, 0, None, 128, True),
+    (2, 2, 2, 130, 257, False, False, 0, 0.0, 64, True),
+]
+
+
+def _qq_id(c):
+    return _fwd_id(c[:10]) + ("pv8" if c[10] else "")
+
+
+def _two_pass_and_fused(inp, q, k, v, signs, scale, causal, pv8, out_dtype):
+    sd = _signs_dev(signs)
+    qc, qs = binding.quantize_fp8(q, sd)
+    kc, ks = binding.quantize_fp8(k, sd)
+    if pv8:
+        vt, vs = binding.quantize_vt_fp8(v)
+        ref = binding.forward_fp8_pv(qc, qs, kc, ks, vt, vs, scale, causal, out_dtype=out_dtype)
+        got = binding.forward_fp8_quantize_q(q, kc, ks, vt, scale, causal, signs=sd, v_scales=vs, out_dtype=out_dtype)
+    else:
+        ref = binding.forward_fp8(qc, qs, kc, ks, v, scale, causal, out_dtype=out_dtype)
+        got = binding.forward_fp8_quantize_q(q, kc, ks, v, scale, causal, signs=sd, out_dtype=out_dtype)
+    return ref, got
+
+
+@pytest.mark.parametrize("case", QQ_CASES, ids=[_qq_id(c) for c in QQ_CASES])
+def test_fwd_fp8_quantize_q_equals_two_passes(case):
+    # the same codes, scales and products as fa_quantize_fp8(Q) followed by
+    # fa_fwd_fp8 / fa_fwd_fp8_pv (whose parity with the oracle the tests
+    # above establish), so O (fp32 and bf16) and L agree bit for bit
+    import torch
+    B, Hq, Hkv, Nq, Nk, causal, with_signs, outl, scale, d, pv8 = case
+    scale = float(np.float32(1 / np.sqrt(d))) if scale is None else scale
+    announce(f"fa_fwd_fp8_quantize_q {_qq_id(case)}")
+    inp = gen(71 + Nq + Nk, B, Hq, Hkv, Nq, Nk, d, outliers=outl)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(9, d) if with_signs else None
+    for od in (torch.float32, torch.bfloat16):
+        (o_ref, l_ref), (o, l) = _two_pass_and_fused(inp, q, k, v, signs, scale, causal, pv8, od)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"O ({od}) differs from the two-pass path"
+        assert torch.equal(l, l_ref), f"L ({od}) differs from the two-pass path"
+
+
+def test_fwd_fp8_quantize_q_against_the_oracle():
+    # one case straight against the oracle's FP8 forward (bf16 V), as
+    # test_fwd_fp8_parity does for the two-pass path
+    import torch
+    B, Hq, Hkv, Nq, Nk, d, causal = 1, 4, 2, 300, 300, 128, True
+    scale = float(np.float32(1 / np.sqrt(d)))
+    announce("fa_fwd_fp8_quantize_q against the oracle")
+    inp = gen(77, B, Hq, Hkv, Nq, Nk, d)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(9, d)
+    sd = _signs_dev(signs)
+    kc, ks = binding.quantize_fp8(k, sd)
+    o, l = binding.forward_fp8_quantize_q(q, kc, ks, v, scale, causal, signs=sd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = ofp8.forward_fp8(inp.q, inp.k, inp.v, scale, causal, signs)
+    oqc, oqs = ofp8.quantize(inp.q, signs)
+    okc, oks = ofp8.quantize(inp.k, signs)
+    O32, L32 = host(o), host(l)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            bound = window_bound(oqc[b, h], oqs[b, h], okc[b, g], oks[b, g], scale, causal)
+            _assert_within(O32[b, h], L32[b, h], O[b, h], L[b, h], np.max(np.abs(inp.v[b, g])), bound, f"head {(b, h)}")
+    assert np.max(np.abs(O32 - O)) <= 1e-2
+    assert np.max(np.abs(L32 - L)) <= 1e-3
+
+
+@pytest.mark.parametrize("pv8", [False, True])
+def test_fwd_fp8_quantize_q_full_size(pv8):
+    # the 2K-key causal workload at full size (B8 H16 d128), both V paths:
+    # bit for bit equal to the two passes
+    import torch
+    w = WORKLOADS["fwd_bf16_causal_b8_h16_n2048_d128"]
+    announce(f"fa_fwd_fp8_quantize_q full size {w.name} pv8={pv8}")
+    inp = gen(w.seed, w.batch, w.n_q_heads, w.n_kv_heads, w.seqlen, w.seqlen, w.head_dim)
+    q, k, v, _ = upload(inp)
+    signs = make_signs(w.seed, w.head_dim)
+    (o_ref, l_ref), (o, l) = _two_pass_and_fused(inp, q, k, v, signs, w.scale, w.causal, pv8, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
