@@ -674,7 +674,7 @@ def _template_args(kernel):
 # Position of the VARLEN / PERSIST / PV8 template argument of each kernel template
 # (fwd_kernel<F32IN, D, CAUSAL, OUTF32, NW, VARLEN, PERSIST>,
 # bwd_dkdv_kernel<D, CAUSAL, GF32, VARLEN, HILO>, bwd_dkdv4_kernel<D, CAUSAL, GF32, VARLEN>,
-# bwd_dq_kernel<D, CAUSAL, VARLEN, NW, HILO>, fwd_fp8_kernel<D, CAUSAL, OUTF32, PV8>).
+# bwd_dq_kernel<D, CAUSAL, VARLEN, NW, HILO>, fwd_fp8_kernel<D, CAUSAL, OUTF32, PV8, QBF16>).
 _VARLEN_ARG = {
     "void fa::fwd_kernel<": 5,
     "void fa::bwd_dkdv_kernel<": 3,
@@ -683,10 +683,14 @@ _VARLEN_ARG = {
 }
 _PERSIST_ARG = {"void fa::fwd_kernel<": 6}
 _PV8_ARG = {"void fa::fwd_fp8_kernel<": 3}
+_QBF16_ARG = {"void fa::fwd_fp8_kernel<": 4}
 
 
 def _call_of(kernel):
     t = _template_args(kernel)
+    for prefix, pos in _QBF16_ARG.items():
+        if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
+            return "fa_fwd_fp8_quantize_q"
     for prefix, pos in _PV8_ARG.items():
         if kernel.startswith(prefix) and len(t) > pos and t[pos] == "true":
             return "fa_fwd_fp8_pv"

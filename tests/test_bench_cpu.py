@@ -43,6 +43,12 @@ def test_kernel_to_entry_point():
     assert bench._call_of("void fa::bwd_dkdv4_kernel<64, true, false, true>(fa::BwdArgs)") == "fa_bwd_varlen"
     assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, false>(fa::FwdArgs)") == "fa_fwd_fp8"
     assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, true>(fa::FwdArgs)") == "fa_fwd_fp8_pv"
+    assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, false, false>(fa::FwdArgs)") == "fa_fwd_fp8"
+    assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, true, false>(fa::FwdArgs)") == "fa_fwd_fp8_pv"
+    assert bench._call_of("void fa::fwd_fp8_kernel<128, true, false, false, true>(fa::FwdArgs)") == \
+        "fa_fwd_fp8_quantize_q"
+    assert bench._call_of("void fa::fwd_fp8_kernel<64, false, true, true, true>(fa::FwdArgs)") == \
+        "fa_fwd_fp8_quantize_q"
     assert bench._call_of("void fa::quantize_vt_fp8_kernel<128>(bool _Accum const*, unsigned char*, float*, int, "
                           "int)") == "fa_quantize_vt_fp8"
     assert bench._call_of("void fa::quantize_fp8_kernel<128>(bool _Accum const*, unsigned char*, float*, "
