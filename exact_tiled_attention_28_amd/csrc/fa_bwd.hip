@@ -453,10 +453,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   using T = DkdvTile<D, HILO>;
   constexpr int BKV = T::BKV, BQ = T::BQ, ROWB = T::ROWB, RC = T::RC, QTILEB = T::QTILEB;
   // Own query half's dV/dK products before the exchange barrier: +2.5-5 % on
-  // causal d = 128 backward shapes on MI355X; the non-causal instance keeps
-  // them after it (-0.5 %, one more spilled register), and so does HILO,
-  // which reads its own P and dS back from the exchange.
-  constexpr bool OWN_FIRST = CAUSAL && !HILO;
+  // causal d = 128 backward shapes on MI355X and +1.5-3 % non-causal; HILO
+  // keeps them after it (it reads its own P and dS back from the exchange).
+  constexpr bool OWN_FIRST = !HILO;
   constexpr int QCPW = T::QCPW, XB = T::XB;
   constexpr int NKK = D / 16, NDH = D / 64;  // NDH: 32-wide head-dim blocks per half
 
@@ -464,11 +463,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Q/dO buffers every LDS access names its buffer at compile time, so the
   // compiler can tell that the reads of one buffer never alias the HBM->LDS
   // loads in flight into the other and does not wait for them.
+  // Each buffer holds its Q tile and then its dO tile. The compiler lays the
+  // static LDS objects out by decreasing alignment, so the two buffers come
+  // first (at 0 and 32 KiB) and every tile address is a loop-invariant
+  // per-lane offset plus a constant that fits the 16-bit immediate offset of
+  // the LDS reads: no address arithmetic per read (-30 VALU instructions per
+  // Q block, +3-4 % on causal d = 128 backward shapes).
+  __shared__ __attribute__((aligned(1024))) char sQD0[2 * QTILEB];
+  __shared__ __attribute__((aligned(1024))) char sQD1[2 * QTILEB];
   __shared__ __attribute__((aligned(16))) char sX[T::NW * XB];
-  __shared__ __attribute__((aligned(16))) char sQ0[QTILEB];
-  __shared__ __attribute__((aligned(16))) char sQ1[QTILEB];
-  __shared__ __attribute__((aligned(16))) char sDO0[QTILEB];
-  __shared__ __attribute__((aligned(16))) char sDO1[QTILEB];
+  char* const sQ0 = sQD0;
+  char* const sDO0 = sQD0 + QTILEB;
+  char* const sQ1 = sQD1;
+  char* const sDO1 = sQD1 + QTILEB;
   __shared__ __attribute__((aligned(16))) float sL0[BQ];
   __shared__ __attribute__((aligned(16))) float sL1[BQ];
   __shared__ __attribute__((aligned(16))) float sD0[BQ];
@@ -533,16 +540,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   // Per-lane LDS offsets.
-  int roff[NKK];  // row reads: row l32 of a 32-row block, head-dim step kk
+  // row reads: row 32*h + l32 of a Q block, head-dim step kk (the swizzle
+  // depends on the row mod 16, so the half's offset is part of it)
+  int roff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) roff[kk] = tile_off<RC>(l32, (kk * 16 + 8 * g) * 2);
-  int troff[NDH][2];  // transpose reads: this wavefront's head-dim blocks, half hh
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = tile_off<RC>(32 * h + l32, (kk * 16 + 8 * g) * 2);
+  // transpose reads: this wavefront's head-dim blocks db, rows +8*e of the
+  // query half of its own scores (ptr = 0) or of its partner's (ptr = 1)
+  int troff[2][NDH][2];
 #pragma unroll
-  for (int db = 0; db < NDH; ++db)
+  for (int ptr = 0; ptr < 2; ++ptr)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      troff[db][hh] = tile_off<RC>(4 * g + 8 * hh + (j16 >> 2),
-                                   ((h * NDH + db) * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
+    for (int db = 0; db < NDH; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        troff[ptr][db][e] = tile_off<RC>(32 * (h ^ ptr) + 4 * g + 8 * e + (j16 >> 2),
+                                         ((h * NDH + db) * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3)) * 2);
 
   f32x16 dkacc[NDH], dvacc[NDH];
 #pragma unroll
@@ -617,14 +630,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
                     bf16x8 (&pb)[2], bf16x8 (&dsb)[2], bf16x8 (&pl)[2], bf16x8 (&dsl)[2])
                     __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* qRows = tQ + h * 32 * ROWB;
-    const char* oRows = tDO + h * 32 * ROWB;
+    const char* qRows = tQ;
+    const char* oRows = tDO;
     // S = Q K^T (query rows from LDS, K rows in registers, one key per lane)
     f32x16 s = f32x16{};
-    if constexpr (CAUSAL || D == 64) {
+    {
       // The Q operand of step kk + 1 is read before the product of step kk,
-      // order pinned (measured 1-2 % faster; the d = 128 non-causal instance
-      // keeps the compiler's order, which was 0-1 % faster there).
+      // order pinned (measured 1-2 % faster).
       bf16x8 qa[2];
       qa[0] = *(const bf16x8*)(qRows + roff[0]);
 #pragma unroll
@@ -638,9 +650,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (kk + 2 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16(*(const bf16x8*)(qRows + roff[kk]), kf[kk], s);
     }
     // P = exp2(S c - L log2 e). Masked: query q0 + 32h + 8*a4 + 4g + e sees
     // this lane's key iff 8*a4 + e >= tq (no query if the key is past the end
@@ -686,18 +695,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of half hh, for
-  // this wavefront's head-dim half (with HILO, also the products of the low
-  // halves pl, dsl; unused otherwise).
-  auto grads = [&](int hh, const char* tQ, const char* tDO, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2],
+  // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows of the
+  // wavefront's own query half (ptr = 0) or its partner's (ptr = 1), for this
+  // wavefront's head-dim half (with HILO, also the products of the low halves
+  // pl, dsl; unused otherwise).
+  auto grads = [&](int ptr, const char* tQ, const char* tDO, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2],
                    const bf16x8 (&pl)[2], const bf16x8 (&dsl)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDH; ++db) {
-        const char* base = tDO + (32 * hh + 16 * t) * ROWB;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+        const char* base = tDO + 16 * t * ROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[ptr][db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[ptr][db][1]));
         dvacc[db] = mfma_bf16(cat4(lo, hi), pb[t], dvacc[db]);
         if constexpr (HILO) dvacc[db] = mfma_bf16(cat4(lo, hi), pl[t], dvacc[db]);
       }
@@ -705,9 +715,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDH; ++db) {
-        const char* base = tQ + (32 * hh + 16 * t) * ROWB;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][0]));
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[db][1]));
+        const char* base = tQ + 16 * t * ROWB;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[ptr][db][0]));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS short4v*)(base + troff[ptr][db][1]));
         dkacc[db] = mfma_bf16(cat4(lo, hi), dsb[t], dkacc[db]);
         if constexpr (HILO) dkacc[db] = mfma_bf16(cat4(lo, hi), dsl[t], dkacc[db]);
       }
@@ -759,7 +769,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       // The products of the wavefront's own query half need nothing from
       // its partner: with OWN_FIRST they run before the exchange barrier,
       // which then waits only for what is left of the partner's scores.
-      if constexpr (OWN_FIRST) grads(h, tQ, tDO, pb, dsb, pl, dsl);
+      if constexpr (OWN_FIRST) grads(0, tQ, tDO, pb, dsb, pl, dsl);
     }
     // The exchange needs only the P/dS writes to have landed; the Q/dO tiles
     // of the next block stay in flight across this barrier.
@@ -769,12 +779,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       // With HILO the wavefront's own P and dS are read back from the
       // exchange rather than kept in registers across the barrier.
       if constexpr (HILO) read_x(myX, pb, dsb, pl, dsl);
-      grads(h, tQ, tDO, pb, dsb, pl, dsl);
+      grads(0, tQ, tDO, pb, dsb, pl, dsl);
     }
     if (h ? act0 : act1) {
       bf16x8 ppb[2], pds[2], ppl[2], pdsl[2];
       read_x(ptX, ppb, pds, ppl, pdsl);
-      grads(h ^ 1, tQ, tDO, ppb, pds, ppl, pdsl);
+      grads(1, tQ, tDO, ppb, pds, ppl, pdsl);
     }
     if (has_next) store_ld(nL, nD);
     wait_vmem();
