@@ -864,6 +864,11 @@ SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", 
                "SQ_ACTIVE_INST_VALU")
 
 
+# The second counter pass: LDS activity and where the wavefronts wait.
+LDS_WAIT_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                     "SQ_WAIT_INST_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_BUSY_CYCLES")
+
+
 def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024, n_cu=256):
     """Per-kernel averages of one rocprofv3 --pmc run of SQ_COUNTERS: clock
     (GRBM_GUI_ACTIVE, summed over the n_xcd XCD instances, over the
@@ -873,7 +878,14 @@ def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024, n_cu=256):
     co-execution (SQ_VALU_MFMA_COEXEC_CYCLES, cycles in which a SIMD issued a
     VALU instruction while its MFMA unit was busy, as a share of the MFMA
     busy cycles), instructions per wavefront and LDS bank-conflict cycles.
-    Counters absent from the run read as zero."""
+    Counters absent from the run read as zero. A run of LDS_WAIT_COUNTERS
+    (recognised by SQ_LDS_IDX_ACTIVE) is summarised instead as: LDS busy
+    (rocprofv3's LdsUtil expression: SQ_LDS_IDX_ACTIVE / n_cu / cycles),
+    the shares of the wavefronts' lifetime (SQ_WAVE_CYCLES) spent waiting on
+    a dependency or s_waitcnt/barrier (SQ_WAIT_ANY), waiting to issue
+    (SQ_WAIT_INST_ANY) and waiting to issue an LDS instruction
+    (SQ_WAIT_INST_LDS), all in the same quad-cycle unit, and the cycles the
+    LDS data FIFO was full per CU."""
     import collections
     import csv
     import glob
@@ -887,6 +899,25 @@ def summarize_pmc(prof_dir, n_xcd=8, n_simd=1024, n_cu=256):
             d = disp[r["Kernel_Name"]][r["Dispatch_Id"]]
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    if any("SQ_LDS_IDX_ACTIVE" in d for ds in disp.values() for d in ds.values()):
+        print("| kernel | entry point | dispatches | µs | clock GHz | LDS busy % | wave cycles / wave | waiting % | "
+              "waiting to issue % | waiting to issue LDS % | LDS data FIFO full cycles / CU |")
+        print("|---|---|---|---|---|---|---|---|---|---|---|")
+        for name, ds in disp.items():
+            call = _call_of(name)
+            if call is None:
+                continue
+            n = len(ds)
+            avg = {k: sum(d.get(k, 0.0) for d in ds.values()) / n for k in ("_ns",) + LDS_WAIT_COUNTERS}
+            cyc = avg["GRBM_GUI_ACTIVE"] / n_xcd
+            waves = max(avg["SQ_WAVES"], 1.0)
+            wc = max(avg["SQ_WAVE_CYCLES"], 1.0)
+            lds_busy = 100.0 * avg["SQ_LDS_IDX_ACTIVE"] / n_cu / cyc if cyc else 0.0
+            print(f"| `{name}` | {call} | {n} | {avg['_ns'] / 1e3:.1f} | {cyc / avg['_ns']:.2f} | {lds_busy:.1f} | "
+                  f"{4 * wc / waves:.0f} | {100 * avg['SQ_WAIT_ANY'] / wc:.1f} | "
+                  f"{100 * avg['SQ_WAIT_INST_ANY'] / wc:.1f} | {100 * avg['SQ_WAIT_INST_LDS'] / wc:.1f} | "
+                  f"{avg['SQ_LDS_DATA_FIFO_FULL'] / n_cu:.0f} |")
+        return
     print("| kernel | entry point | dispatches | µs | clock GHz | MFMA busy % | VALU busy % | co-exec % of MFMA "
           "busy | VALU instr / wave | MFMA instr / wave | VALU / MFMA | LDS instr / wave | LDS bank-conflict "
           "cycles |")

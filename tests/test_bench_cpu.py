@@ -164,6 +164,29 @@ def test_summarize_pmc_reports_coexec_and_valu_busy(tmp_path, capsys):
     assert cells[10] == "4.00"  # VALU per MFMA
 
 
+def test_summarize_pmc_reports_lds_busy_and_waits(tmp_path, capsys):
+    path = tmp_path / "sq2" / "bench_counter_collection.csv"
+    os.makedirs(path.parent)
+    fields = FIELDS + ["Start_Timestamp", "End_Timestamp"]
+    # 2000 cycles per XCD; LDS busy on a quarter of 256 CUs x 2000 cycles; 100 waves of 400 quad-cycles
+    vals = {"GRBM_GUI_ACTIVE": 16000, "SQ_WAVES": 100, "SQ_WAVE_CYCLES": 40000, "SQ_WAIT_ANY": 10000,
+            "SQ_WAIT_INST_ANY": 12000, "SQ_WAIT_INST_LDS": 2000, "SQ_LDS_IDX_ACTIVE": 128000,
+            "SQ_LDS_DATA_FIFO_FULL": 2560, "SQ_BUSY_CYCLES": 2000}
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        for c, v in vals.items():
+            w.writerow({"Correlation_Id": 1, "Dispatch_Id": 1, "Kernel_Name": DKDV, "Counter_Name": c,
+                        "Counter_Value": v, "Start_Timestamp": 0, "End_Timestamp": 1000})
+    bench.summarize_pmc(str(path.parent))
+    out = capsys.readouterr().out
+    assert "LDS busy %" in out
+    row = [line for line in out.splitlines() if DKDV in line][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    # clock, LDS busy, wave cycles per wave, waiting, waiting to issue, waiting to issue LDS, FIFO full per CU
+    assert cells[4:11] == ["2.00", "25.0", "1600", "25.0", "30.0", "5.0", "10"]
+
+
 # `amd-smi metric -g 0 --clock --json` output as printed on an idle MI355X
 # (trimmed to two XCDs and one other clock domain).
 AMD_SMI_CLOCK = """{
