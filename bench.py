@@ -106,6 +106,9 @@ def parse(argv=None):
                         "under profiles/, which the benchmark line reads)")
     p.add_argument("--summarize-pmc", default=None, metavar="DIR",
                    help="summarise a rocprofv3 --pmc run of the SQ counters under DIR (no GPU needed)")
+    p.add_argument("--machine-limits", action="store_true",
+                   help="run the in-bounds microbenchmarks of tests/hw/machine_limits.hip (matrix-core rate, exp "
+                        "beside it, LDS read patterns, shader clock) and print their table")
     p.add_argument("--calibration-mib", type=int, default=256, help="copy size used by the counter runs")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, copy a MIB-MiB buffer 3 times (a plain copy kernel of known size, to "
@@ -977,6 +980,10 @@ def main():
         return summarize_profiles(args.summarize_profiles, args.calibration_mib, args.profile_out)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.machine_limits:
+        from tests.hw import machine_limits
+        print(machine_limits.markdown(machine_limits.run()))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the attention path runs on one GPU)", file=sys.stderr)

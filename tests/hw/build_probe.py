@@ -1,5 +1,6 @@
-"""Build the test helper tests/hw/libfp8probe.so (gfx950) from
-fp8_mfma_probe.hip; called by the repository's build entry point."""
+"""Build the test helpers tests/hw/libfp8probe.so (gfx950) from
+fp8_mfma_probe.hip and tests/hw/libmachlimits.so from machine_limits.hip;
+called by the repository's build entry point."""
 
 import os
 import subprocess
@@ -16,4 +17,6 @@ def build() -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("building the FP8 probe failed:\n" + res.stdout + res.stderr)
+    from tests.hw.machine_limits import build as build_machine_limits
+    build_machine_limits()
     return LIB
