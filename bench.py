@@ -54,7 +54,7 @@ sys.path.insert(0, ROOT)
 from exact_tiled_attention_28_amd import binding  # noqa: E402
 from exact_tiled_attention_28_amd.inputs import make_inputs  # noqa: E402
 from exact_tiled_attention_28_amd.workloads import (  # noqa: E402
-    MI355X_BF16_PEAK_TFLOPS, WORKLOAD_ORDER, WORKLOADS, bwd_bytes, bwd_flops, fwd_bytes, fwd_flops,
+    MI355X_BF16_PEAK_TFLOPS, MI355X_HBM_GBPS, WORKLOAD_ORDER, WORKLOADS, bwd_bytes, bwd_flops, fwd_bytes, fwd_flops,
     workload_bytes, workload_flops)
 
 METRIC = "attention fwd/bwd TFLOPS (causal-adjusted) and % of MI355X bf16 MFMA peak"
@@ -457,14 +457,17 @@ SWEEP_TOKENS, SWEEP_HD = 16384, 2048  # B * N tokens and Hq * d per shape
 
 def bench_sweep(args):
     """Throughput of fa_fwd (bf16 O) and fa_bwd (fp32 dQ, bf16 dK/dV) over
-    head dim 64/128, N = 1K..32K, causal and non-causal, MHA and GQA (G = 4),
+    head dim 64/128, N = 128..32K, causal and non-causal, MHA and GQA (G = 4),
     with B = max(1, 16384 / N) and Hq = 2048 / d: N(0, 1) bf16 inputs drawn on
     the GPU from a seeded generator. One JSON line per shape (median of
-    --steps timed calls after --warmup), then a summary line."""
+    --steps timed calls after --warmup): TFLOP/s and % of the bf16 peak, and
+    the algorithmic HBM rate (fwd_bytes / bwd_bytes over the time) with its %
+    of 8 TB/s, the bound that matters for the short sequences; then a summary
+    line."""
     import torch
     rows = []
     for d in (64, 128):
-        for n in (1024, 2048, 4096, 8192, 16384, 32768):
+        for n in (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
             for causal in (True, False):
                 for group in (1, 4):
                     B, Hq = max(1, SWEEP_TOKENS // n), SWEEP_HD // d
@@ -506,11 +509,18 @@ def bench_sweep(args):
                            "bwd_ms": round(bm, 4), "bwd_tflops": round(bfl / (bm * 1e-3) / 1e12, 1)}
                     row["fwd_pct"] = round(100 * row["fwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 1)
                     row["bwd_pct"] = round(100 * row["bwd_tflops"] / MI355X_BF16_PEAK_TFLOPS, 1)
+                    fb, bb = fwd_bytes(B, Hq, Hkv, n, n, d), bwd_bytes(B, Hq, Hkv, n, n, d)
+                    row["fwd_gbps"] = round(fb / (fm * 1e-3) / 1e9, 1)
+                    row["bwd_gbps"] = round(bb / (bm * 1e-3) / 1e9, 1)
+                    row["fwd_pct_hbm"] = round(100 * row["fwd_gbps"] / MI355X_HBM_GBPS, 1)
+                    row["bwd_pct_hbm"] = round(100 * row["bwd_gbps"] / MI355X_HBM_GBPS, 1)
                     rows.append(row)
                     print(json.dumps(row), flush=True)
                     del q, k, v, do, o, lse, dq, dk, dv, ws
     best = max(rows, key=lambda r: r["fwd_tflops"] if r["causal"] and r["d"] == 128 else 0)
-    print(json.dumps({"sweep_shapes": len(rows), "best_causal_d128_fwd": best}), flush=True)
+    best_short = max(rows, key=lambda r: r["fwd_gbps"] if r["N"] <= 512 else 0)
+    print(json.dumps({"sweep_shapes": len(rows), "best_causal_d128_fwd": best, "best_short_fwd_gbps": best_short}),
+          flush=True)
 
 
 def bench_persistent(args):
