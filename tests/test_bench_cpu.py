@@ -6,6 +6,7 @@ the refusal of more than one GPU."""
 
 import csv
 import json
+import ctypes
 import os
 import subprocess
 import sys
@@ -251,3 +252,19 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_machine_limit_probes_export_and_reject_bad_arguments():
+    # the helper behind `bench.py --machine-limits`: it loads without a GPU,
+    # exports its three launchers and refuses bad arguments before any launch
+    from tests.hw import machine_limits
+    if not os.path.exists(machine_limits.LIB):
+        machine_limits.build()
+    lib = machine_limits._lib()
+    assert lib.ml_mfma(None, 256, 10, None, None) == -1
+    assert lib.ml_exp(None, 256, 10, 1, 1, None, None) == -1
+    assert lib.ml_lds(None, 256, 10, 0, None, None) == -1
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails its argument check
+    assert lib.ml_mfma(buf, 0, 10, buf, None) == -1
+    assert lib.ml_exp(buf, 256, 10, 1, 5, buf, None) == -1
+    assert lib.ml_lds(buf, 256, 10, 2, buf, None) == -1
