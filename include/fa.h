@@ -29,7 +29,9 @@
  *    work is enqueued on it; the call returns without synchronising.
  *  - Ownership: the caller allocates and frees every buffer and owns the
  *    stream. The library never allocates, frees or synchronises, and keeps no
- *    state between calls except a thread-local error message.
+ *    state between calls except a thread-local error message; a call only
+ *    enqueues kernels, so fa_fwd and fa_bwd can be captured into a HIP graph
+ *    on a capturing stream and replayed.
  *  - Errors: argument problems are detected on the host before anything is
  *    enqueued, and leave every output untouched. A launch failure returns
  *    FA_ERR_HIP. Faults inside a kernel surface at the caller's next
