@@ -1446,13 +1446,21 @@ static hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream) {
 // MI355X over causal, GQA and non-causal shapes up to 8K keys, level at 16K
 // non-causal), else, and with HILO, the eight-wavefront kernel with the P/dS
 // exchange (at d = 128 the four-wavefront layout reads 1.6x the LDS bytes
-// per flop and measured between -7 % and +4 % against it).
+// per flop). At d = 128 the four-wavefront kernel still serves short causal
+// rows without query-head groups, where its two independent workgroups per
+// CU outweigh the LDS bytes: whole backward +5 % at 1024 keys and +9-12 % at
+// 512, but -1 to -2 % at 2048 and -6 % at 4096.
+constexpr int kDkdv4MaxKeysD128 = 1024;
+
 template <int D, bool CAUSAL, bool GF32, bool HILO>
 static hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  if constexpr (!HILO && D == 64) {
-    const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, Dkdv4Tile<D>::BKV);
-    hipLaunchKernelGGL((bwd_dkdv4_kernel<D, CAUSAL, GF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
+  if constexpr (!HILO) {
+    if (D == 64 || (CAUSAL && a.G == 1 && a.Nk <= kDkdv4MaxKeysD128)) {
+      const long long blocks = (long long)a.B * a.Hkv * ceil_div(a.Nk, Dkdv4Tile<D>::BKV);
+      hipLaunchKernelGGL((bwd_dkdv4_kernel<D, CAUSAL, GF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+      return hipGetLastError();
+    }
   }
   using T = DkdvTile<D, HILO>;
   auto kern = bwd_dkdv_kernel<D, CAUSAL, GF32, false, HILO>;
