@@ -114,6 +114,24 @@ def test_bwd_wide_dq_parity(case, scheme):
     assert np.max(np.abs(Dv - oracle.row_dot(inp.do, O))) <= 1e-4
 
 
+# Causal d = 128 rows without query-head groups run the four-wavefront dK/dV
+# kernel up to 1024 keys and the eight-wavefront one above: both sides of
+# that switch, with a ragged last key block below it.
+SHORT_ROW_CASES = [(1, 2, 2, 1023, 1023, 128, True), (1, 2, 2, 1024, 1024, 128, True),
+                   (1, 2, 2, 1025, 1025, 128, True)]
+
+
+@pytest.mark.parametrize("case", SHORT_ROW_CASES, ids=[_cid(c) for c in SHORT_ROW_CASES])
+def test_bwd_short_row_dispatch_parity(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    announce(f"bwd short-row dispatch {case}")
+    inp = gen(700 + Nq, B, Hq, Hkv, Nq, Nk, d, with_do=True)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    O, L, dQ, dK, dV, Dv = run_fwd_bwd(inp, scale, causal)
+    dQr, dKr, dVr = oracle.backward(inp.q, inp.k, inp.v, inp.do, scale, causal)
+    check_flat(dQ, dK, dV, dQr, dKr, dVr, _cid(case))
+
+
 @pytest.mark.parametrize("scheme", SCHEMES)
 def test_bwd_bf16_grads(scheme):
     announce(f"bwd bf16 grads scheme={scheme}")
