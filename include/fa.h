@@ -45,9 +45,10 @@
  *    row does not reach the causal rows before it. Where a product spans a
  *    whole tile, a NaN also reaches outputs of the same tile through a zero
  *    factor: a NaN in query row i sets dK_j to NaN for the keys i < j <=
- *    32 * floor(i / 32) + 31 as well (64 * floor(i / 64) + 63 at head_dim 64
- *    with FA_PRECISION_BF16): the dK/dV pass multiplies aligned 32-row
- *    (64-row) blocks of Q, and 0 * NaN is NaN.
+ *    32 * floor(i / 32) + 31 as well (64 * floor(i / 64) + 63 with
+ *    FA_PRECISION_BF16 at head_dim 64, and at head_dim 128 for causal calls
+ *    with n_q_heads == n_kv_heads and seqlen_k <= 1024): the dK/dV pass
+ *    multiplies aligned 32-row (64-row) blocks of Q, and 0 * NaN is NaN.
  */
 #ifndef FA_H_
 #define FA_H_

@@ -214,22 +214,25 @@ def test_bwd_with_bf16_o(case):
     check_flat(dQ, dK, dV, dQr, dKr, dVr, f"{_cid(case)} bf16 O")
 
 
+@pytest.mark.parametrize("hkv", [1, 2], ids=["gqa", "mha"])
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("hilo", [False, True], ids=["bf16", "hilo"])
-def test_bwd_nan_in_one_q_row(hilo, d):
+def test_bwd_nan_in_one_q_row(hilo, d, hkv):
     """A NaN in query row i of one head (causal, the K/V head shared by two
     query heads). The outputs that depend on that row become NaN: O_i, L_i,
     D_i, dQ_i, and dV_j, dK_j of every key j <= i it sees. The K/V-outer pass
     forms dK_j = s sum_i dS_ij Q_i over aligned blocks of query rows (64 rows
-    at head dim 64 with bf16 P and dS, else 32 rows), so a NaN in Q_i (and in
+    at head dim 64 with bf16 P and dS, and at head dim 128 with bf16 P and dS
+    for causal rows of up to 1024 keys without query-head groups, else 32
+    rows), so a NaN in Q_i (and in
     D_i, through dS_ij = P_ij (dP_ij - D_i) with P_ij = 0) also reaches dK_j
     for the keys after i up to the end of i's block, j <= 64 floor(i / 64) + 63
     (j <= 32 floor(i / 32) + 31), which do not depend on it. Every other output
     is finite and matches the oracle evaluated with the row set to zero."""
     import torch
-    B, Hq, Hkv, N = 1, 2, 1, 300
+    B, Hq, Hkv, N = 1, 2, hkv, 300
     i = 77
-    announce(f"bwd NaN Q row hilo={hilo} d={d}")
+    announce(f"bwd NaN Q row hilo={hilo} d={d} Hkv={hkv}")
     inp = gen(71, B, Hq, Hkv, N, N, d, with_do=True)
     clean_q = inp.q.copy()
     clean_q[0, 1, i] = 0.0
@@ -244,11 +247,12 @@ def test_bwd_nan_in_one_q_row(hilo, d):
     rows_nan = np.zeros((B, Hq, N), dtype=bool)
     rows_nan[0, 1, i] = True
     keys = np.arange(N)
+    kvh = 1 // (Hq // Hkv)  # the K/V head of query head 1
     dv_nan = np.zeros((B, Hkv, N), dtype=bool)
-    dv_nan[0, 0] = keys <= i
+    dv_nan[0, kvh] = keys <= i
     dk_nan = np.zeros((B, Hkv, N), dtype=bool)
-    blk = 64 if (d == 64 and not hilo) else 32
-    dk_nan[0, 0] = keys <= blk * (i // blk) + blk - 1
+    blk = 64 if (not hilo and (d == 64 or Hq == Hkv)) else 32
+    dk_nan[0, kvh] = keys <= blk * (i // blk) + blk - 1
     assert np.array_equal(np.isnan(Dv), rows_nan)
     assert np.array_equal(np.isnan(dQ).any(axis=-1), rows_nan) and np.all(np.isnan(dQ[rows_nan]))
     assert np.array_equal(np.isnan(dV).any(axis=-1), dv_nan) and np.all(np.isnan(dV[dv_nan]))
